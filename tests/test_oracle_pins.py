@@ -1,0 +1,378 @@
+"""Pins of the CPU oracle to things other than itself: closed forms, special cases,
+brute force on tiny inputs and invariants.  CPU only."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from synth import workloads as SW
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- EMA (R3)
+@pytest.mark.parametrize("beta", [0.9, 0.999, 0.5])
+def test_ema_closed_form_constant_query(beta):
+    """Constant q from zero gives s_t = (1 - beta^t) q (within the float32 rounding of t steps)."""
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal(64).astype(np.float32)
+    s = np.zeros(64, np.float32)
+    for t in range(1, 201):
+        s = O.ema_update(s, q, beta)
+        b = float(np.float32(beta))
+        want = (1.0 - b ** t) * q.astype(np.float64)
+        err = np.abs(s.astype(np.float64) - want)
+        assert np.all(err <= (t + 1) * 2.0 ** -23 * np.abs(q) * 2), (t, err.max())
+
+
+def test_ema_special_cases():
+    rng = np.random.default_rng(2)
+    s0 = rng.standard_normal(32).astype(np.float32)
+    q = rng.standard_normal(32).astype(np.float32)
+    assert np.array_equal(O.ema_update(s0, q, 0.0), q)          # beta 0: the last query
+    assert np.array_equal(O.ema_update(s0, q, 1.0), s0)         # beta 1: frozen
+    # beta 1/2 with values whose halves and sums are exact in float32
+    assert np.array_equal(O.ema_update(np.float32([1.0, -6.0]), np.float32([3.0, 2.0]), 0.5),
+                          np.float32([2.0, -2.0]))
+    assert O.ema_update(s0, q, 0.9).dtype == np.float32
+
+
+def test_ema_one_minus_beta_is_float32_difference():
+    """(1 - beta) is formed in float32: with s = 0 and q = 1 the first update is exactly
+    1 - float32(beta), which for beta = 0.999 differs from float32(0.001)."""
+    one = np.ones(1, np.float32)
+    out = O.ema_update(np.zeros(1, np.float32), one, 0.999)[0]
+    assert out == np.float32(1.0) - np.float32(0.999)
+    assert out != np.float32(0.001)
+
+
+def test_ema_run_matches_stepwise_and_bias():
+    """With beta_S = beta_L the two summaries coincide; the short one forgets faster."""
+    rng = np.random.default_rng(3)
+    qs = rng.standard_normal((50, 3, 16)).astype(np.float32)
+    s, l_ = O.ema_run(qs, "f32", 0.9, 0.9)
+    assert np.array_equal(s, l_)
+    s, l_ = O.ema_run(np.ones((32, 1, 4), np.float32), "f32", 0.9, 0.999)
+    # closed forms 1 - 0.9^32 and 1 - 0.999^32
+    assert abs(float(s[0, 0]) - (1 - 0.9 ** 32)) < 1e-5
+    assert abs(float(l_[0, 0]) - (1 - 0.999 ** 32)) < 1e-5
+
+
+# ----------------------------------------------------------------------------- RoPE (R4)
+def test_rope_identity_and_quarter_turn():
+    rng = np.random.default_rng(4)
+    s = rng.standard_normal(8)
+    assert np.array_equal(O.rope_rotate(s, None, None), s)
+    assert np.array_equal(O.rope_rotate(s, np.ones(4), np.zeros(4)), s)
+    # quarter turn on every pair: (x1, x2) -> (-x2, x1)
+    out = O.rope_rotate(s, np.zeros(4), np.ones(4))
+    assert np.array_equal(out, np.concatenate([-s[4:], s[:4]]))
+
+
+def test_rope_norm_and_angle_addition():
+    rng = np.random.default_rng(5)
+    d = 64
+    cos, sin = SW.rope_tables(300, d, theta=10000.0)
+    s = rng.standard_normal(d)
+    for pos in (0, 1, 17, 299):
+        out = O.rope_rotate(s, cos[pos], sin[pos])
+        assert abs(np.linalg.norm(out) - np.linalg.norm(s)) < 1e-6 * np.linalg.norm(s)
+    assert np.allclose(O.rope_rotate(s, cos[0], sin[0]), s, rtol=0, atol=0)
+    # rotating by positions a then b equals rotating by a + b (angles add), which fixes
+    # the sign convention of the pair rotation
+    a, b = 37, 101
+    two = O.rope_rotate(O.rope_rotate(s, cos[a], sin[a]), cos[b], sin[b])
+    one = O.rope_rotate(s, cos[a + b], sin[a + b])
+    assert np.allclose(two, one, atol=1e-5)
+
+
+# ----------------------------------------------------------------------------- logits / softmax
+def test_logits_scale_and_layout():
+    d = 16
+    qt = np.zeros((2, d))
+    qt[0, 0] = math.sqrt(d)
+    qt[1, 3] = 2 * math.sqrt(d)
+    k = np.zeros((5, d))
+    k[:, 0] = np.arange(5)
+    k[:, 3] = -1.0
+    lg = O.logits(qt, k)
+    assert lg.shape == (2, 5)
+    assert np.allclose(lg[0], np.arange(5))
+    assert np.allclose(lg[1], -2.0)
+
+
+def test_softmax_uniform_and_shift():
+    M, Z, a = O.softmax_stats(np.full((1, 10), 3.5))
+    assert M[0] == 3.5 and Z[0] == 10.0 and np.allclose(a, 0.1)
+    rng = np.random.default_rng(6)
+    lg = rng.standard_normal((3, 50))
+    _, _, a1 = O.softmax_stats(lg)
+    _, _, a2 = O.softmax_stats(lg + 100.0)
+    assert np.allclose(a1, a2) and np.allclose(a1.sum(-1), 1.0)
+
+
+# ----------------------------------------------------------------------------- working set (R1)
+def test_working_set_uniform_is_ceil_pn():
+    for n, p in [(100, 0.905), (80, 0.853), (1000, 0.9004), (37, 0.51)]:
+        a = np.full(n, 1.0 / n)
+        W, lo, hi = O.working_set(a, p)
+        assert W == math.ceil(p * n), (n, p, W)
+        assert lo == hi == W          # far from a tie
+
+
+def test_working_set_uniform_exact_tie_is_flagged():
+    """n = 80 and p = float32(0.9): p*n sits on an integer, a near-tie by construction."""
+    n = 80
+    p = float(np.float32(0.9))
+    W, lo, hi = O.working_set(np.full(n, 1.0 / n), p)
+    assert lo <= 72 <= hi and lo != hi
+    assert W in (72, 73)
+
+
+def test_working_set_one_hot():
+    lg = np.zeros(500)
+    lg[123] = 60.0
+    _, _, a = O.softmax_stats(lg[None])
+    assert O.working_set(a[0], 0.9)[0] == 1
+    assert O.working_set(a[0], 0.99)[0] == 1
+
+
+@pytest.mark.parametrize("s,n,p", [(1.1, 1000, 0.9), (0.8, 500, 0.9), (1.6, 4000, 0.99), (2.0, 64, 0.5)])
+def test_working_set_zipf_closed_form(s, n, p):
+    """a_i proportional to i^-s: W = min m with H_{m,s} / H_{n,s} >= p (generalised harmonic numbers)."""
+    ranks = np.arange(1, n + 1, dtype=np.float64)
+    lg = -s * np.log(ranks)
+    rng = np.random.default_rng(7)
+    lg = lg[rng.permutation(n)]
+    _, _, a = O.softmax_stats(lg[None])
+    H = [0.0]
+    for i in range(1, n + 1):
+        H.append(math.fsum([H[-1], i ** -s]))
+    Hn = H[n]
+    want = next(m for m in range(1, n + 1) if H[m] / Hn >= p)
+    W, lo, hi = O.working_set(a[0], p)
+    assert lo <= want <= hi
+    if lo == hi:
+        assert W == want
+
+
+def test_working_set_brute_force_small():
+    """For n <= 10 the smallest subset reaching mass p (over all 2^n subsets) has W elements."""
+    rng = np.random.default_rng(8)
+    for trial in range(200):
+        n = int(rng.integers(1, 11))
+        a = rng.exponential(size=n) ** rng.uniform(0.5, 3)
+        a /= a.sum()
+        p = float(rng.uniform(0.05, 0.999))
+        best = n
+        for m in range(1, n + 1):
+            if any(sum(a[list(c)]) >= p for c in itertools.combinations(range(n), m)):
+                best = m
+                break
+        W, lo, hi = O.working_set(a, p)
+        assert lo <= best <= hi, (a, p)
+        if lo == hi:
+            assert W == best
+
+
+def test_working_set_limits_and_monotone():
+    rng = np.random.default_rng(9)
+    a = rng.exponential(size=300)
+    a /= a.sum()
+    assert O.working_set(a, 1.0)[0] == 300
+    assert O.working_set(a, 1.5)[0] == 300
+    assert O.working_set(a, 0.0)[0] == 1
+    ws = [O.working_set(a, p)[0] for p in np.linspace(0.01, 0.999, 60)]
+    assert all(x <= y for x, y in zip(ws, ws[1:]))
+    assert O.working_set(np.zeros(0), 0.9) == (0, 0, 0)
+
+
+# ----------------------------------------------------------------------------- decision (R2)
+def test_decide_sign_and_tau():
+    ws = np.array([[10, 20], [30, 40]])
+    wl = np.array([[10, 20], [30, 39]])
+    assert O.decide(ws, wl, 0) == (1, O.DECISION_GROW)
+    assert O.decide(ws, wl, 1) == (1, O.DECISION_COMPACT)
+    assert O.decide(wl, ws, 0) == (-1, O.DECISION_COMPACT)
+    assert O.decide(ws, ws, 0) == (0, O.DECISION_COMPACT)      # a tie compacts
+
+
+def test_equal_betas_always_compact():
+    """beta_S == beta_L makes the two summaries identical, so delta = 0 and every request compacts."""
+    wl = SW.config1(seed=1001)
+    s, l_ = O.ema_run(wl.queries, wl.q_dtype, 0.9, 0.9)
+    res = O.boundary_step(wl, s, l_, wl.params)
+    assert res.delta[0] == 0 and res.decision[0] == O.DECISION_COMPACT
+
+
+# ----------------------------------------------------------------------------- keep-set (R5, R6)
+def test_keep_set_invariants_random():
+    rng = np.random.default_rng(10)
+    for _ in range(100):
+        n = int(rng.integers(2, 200))
+        k = int(rng.integers(1, n + 1))
+        nl = int(rng.integers(0, n + 2))
+        imp = rng.exponential(size=n)
+        kept, ev, near = O.keep_set(imp, k, nl)
+        assert kept.size == k and ev.size == n - k
+        assert np.array_equal(np.sort(np.concatenate([kept, ev])), np.arange(n))
+        assert np.all(np.diff(kept) > 0)
+        local = np.arange(n - min(nl, k), n)
+        assert np.all(np.isin(local, kept))
+        nonlocal_kept = np.setdiff1d(kept, local)
+        if ev.size and nonlocal_kept.size:
+            assert imp[nonlocal_kept].min() >= imp[ev].max()
+        assert O.keep_set_valid(ev, imp, k, nl)
+
+
+def test_keep_set_brute_force_small():
+    """Top-(k - local) by importance equals the candidate subset with the largest total importance."""
+    rng = np.random.default_rng(11)
+    for _ in range(100):
+        n = int(rng.integers(2, 11))
+        k = int(rng.integers(1, n + 1))
+        nl = int(rng.integers(0, 3))
+        imp = rng.uniform(size=n)
+        nle = min(nl, k)
+        cand = n - nle
+        best = max(itertools.combinations(range(cand), k - nle), key=lambda c: sum(imp[list(c)]))
+        want = sorted(list(best) + list(range(cand, n)))
+        kept, _, _ = O.keep_set(imp, k, nl)
+        assert list(kept) == want
+
+
+def test_keep_set_ties_keep_recent():
+    imp = np.full(40, 0.025)
+    kept, ev, near = O.keep_set(imp, 30, 0)
+    assert list(ev) == list(range(10))          # the oldest slots go first
+    assert list(kept) == list(range(10, 40))
+    # equal importance except one old heavy slot, which survives
+    imp[2] = 0.5
+    kept, ev, _ = O.keep_set(imp, 30, 4)
+    assert 2 in kept and list(ev) == [0, 1, 3, 4, 5, 6, 7, 8, 9, 10]
+
+
+def test_keep_set_valid_rejects_wrong_sets():
+    imp = np.array([0.5, 0.1, 0.3, 0.05, 0.05])
+    kept, ev, _ = O.keep_set(imp, 3, 0)
+    assert list(ev) == [3, 4]
+    assert O.keep_set_valid(ev, imp, 3, 0)
+    assert not O.keep_set_valid(np.array([1, 4]), imp, 3, 0)
+    assert not O.keep_set_valid(np.array([3]), imp, 3, 0)
+
+
+def test_importance_is_max_over_rows():
+    a = np.array([[0.1, 0.7, 0.2], [0.6, 0.1, 0.3]])
+    assert np.array_equal(O.importance(a), [0.6, 0.7, 0.3])
+
+
+def test_compaction_is_stable_gather():
+    rows = np.arange(20 * 3).reshape(20, 3)
+    kept = np.array([0, 2, 3, 7, 19])
+    out = O.compact_rows(rows, kept)
+    assert np.array_equal(out, rows[kept])
+    # a multiset of original rows, in original order
+    assert all(tuple(r) in {tuple(x) for x in rows} for r in out)
+
+
+# ----------------------------------------------------------------------------- whole step
+def _pool_invariants(res, wl):
+    """refcount == number of page-table references; free stack and referenced pages
+    partition the pool; no duplicates anywhere."""
+    refs = np.zeros(wl.num_pages, np.int64)
+    for b in range(wl.B):
+        for j in range(int(res.n_alloc[b]) + 1):
+            refs[res.page_table[b, j]] += 1
+    assert np.array_equal(refs, res.refcount)
+    free = res.free_stack[: res.free_top]
+    assert np.unique(free).size == free.size
+    assert np.all(refs[free] == 0)
+    assert free.size + np.count_nonzero(refs) == wl.num_pages
+
+
+def test_config1_planted_compaction():
+    wl = SW.config1()
+    s, l_ = O.ema_run(wl.queries, wl.q_dtype, wl.params["beta_s"], wl.params["beta_l"])
+    res = O.boundary_step(wl, s, l_, wl.params)
+    # sharp short summary, flat long one: the recent working set is the smaller
+    assert np.all(res.W[0, 0, :, 0] < res.W[0, 0, :, 1])
+    assert res.decision[0] == O.DECISION_COMPACT and not res.ambiguous[0]
+    assert res.evicted[0].shape == (1, 2, 16)
+    assert res.fill[0] == 0 and res.n_alloc[0] == 4
+    _pool_invariants(res, wl)
+    # the 4 heavy hitters survive
+    k = wl.k_rows[0][0, 0]
+    hh = [i for i in range(80) if np.linalg.norm(k[i]) > 20]
+    assert len(hh) == 4
+    for g in range(2):
+        assert not set(hh) & set(res.evicted[0][0, g].tolist())
+
+
+def test_grow_pops_in_batch_order_and_denial():
+    wl = SW.direct_case(seed=12, B=6, grow_frac=1.0, spare_pages=3)
+    assert wl.free_top == 3
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, wl.params)
+    grows = [b for b in range(wl.B) if res.decision_raw[b] == O.DECISION_GROW]
+    assert len(grows) >= 4
+    popped = [res.page_table[b, wl.n_alloc[b] + 1] for b in grows[:3]]
+    assert popped == [wl.free_stack[2], wl.free_stack[1], wl.free_stack[0]]
+    for b in grows[3:]:
+        assert res.status[b] & O.REQ_GROW_DENIED and res.decision[b] == O.DECISION_COMPACT
+    _pool_invariants(res, wl)
+
+
+def test_copy_on_write_prefix_sharing():
+    wl = SW.direct_case(seed=13, B=4, grow_frac=0.0, prefix_groups=1, prefix_pages=3,
+                        ctx=(60, 120), spare_pages=40, params=dict(SW.PARAMS_DEFAULT, n_local=8))
+    assert wl.refcount[wl.page_table[0, 0]] == 4
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, wl.params)
+    assert res.counters["cow_pages"] > 0
+    _pool_invariants(res, wl)
+    for (b, j, old, new) in res.cow:
+        assert res.page_table[b, j] == new and new != old
+        assert j >= res.e_req[b] // wl.P
+    # kept contents equal the original rows in slot order
+    for b, kn in res.k_new.items():
+        for l in range(wl.L):
+            for g in range(wl.Hkv):
+                ev = set(res.evicted[b][l, g].tolist())
+                kept = [i for i in range(wl.n(b)) if i not in ev]
+                assert np.array_equal(kn[l, g], wl.k_rows[b][l, g][kept])
+
+
+def test_copy_on_write_shortfall_defers():
+    wl = SW.direct_case(seed=14, B=3, grow_frac=0.0, prefix_groups=1, prefix_pages=2,
+                        ctx=(40, 80), spare_pages=0, params=dict(SW.PARAMS_DEFAULT, n_local=4))
+    assert wl.free_top == 0
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, wl.params)
+    deferred = 0
+    for b in range(wl.B):
+        need = [j for j in range(int(res.e_req[b]) // wl.P, int(wl.n_alloc[b]))
+                if wl.refcount[wl.page_table[b, j]] > 1]
+        if need:
+            deferred += 1
+            assert res.status[b] & O.REQ_DEFERRED
+            assert b not in res.k_new and res.fill[b] == wl.P
+            assert np.array_equal(res.page_table[b], wl.page_table[b])
+        else:
+            assert b in res.k_new
+    assert deferred > 0
+    _pool_invariants(res, wl)
+
+
+def test_not_at_boundary_is_untouched():
+    wl = SW.direct_case(seed=15, B=3, fill=[16, 5, 16])
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, wl.params)
+    assert res.status[1] & O.REQ_NOT_AT_BOUNDARY
+    assert res.fill[1] == 5 and 1 not in res.k_new
+
+
+def test_paper_hyperparameters_fixture():
+    g = json.load(open(os.path.join(GOLDEN, "paper_hparams.json")))
+    assert SW.PARAMS_PAPER["beta_s"] == g["beta_s"] and SW.PARAMS_PAPER["beta_l"] == g["beta_l"]
+    assert SW.PARAMS_PAPER["top_p"] == g["top_p"] and SW.PARAMS_PAPER["tau"] == g["tau"]
+    assert SW.PARAMS_PAPER["n_local"] == g["local_retention_quota"]
