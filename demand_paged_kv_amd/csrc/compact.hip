@@ -1,0 +1,519 @@
+// Compaction within the current allocation (GrowPage review on evolve.pub, "Summary":
+// historical KV states are compacted inside the allocation using the maximum of both
+// temporal importance scores; FAQ "Is GrowPage's code available?": local retention
+// quota 64; abstract: page-level integration keeps prefix caching).
+//
+// Launch sequence for one batch (all on the caller's stream, no host round trip):
+//   keep_kernel      per (entry, layer, KV head) unit of a compacting entry: importance
+//                    = max over the 8 softmax rows, exact radix select of the n-k least
+//                    important candidates (ties: older slot first), ascending list.
+//   req_kernel       per entry: first changed slot e (min over units), copy-on-write
+//                    demand = shared pages (refcount > 1) at index >= e / P.
+//   cowplan_kernel   1 block: greedy in batch order -- an entry whose demand fits the
+//                    free stack reserves its pops, otherwise it is deferred.
+//   cowassign_kernel per entry: assign popped pages in ascending page index, rewrite the
+//                    page table, record (old, new).
+//   cowcopy_kernel   copy every (old page, layer, KV head) block of K and V to the new page.
+//   gather_kernel    per unit: in-place stable compaction, slot j <- slot kept[j] for
+//                    j in [e, k), 64 destination rows per step, all reads of a step
+//                    before its writes (destinations never exceed sources).
+//   finalize_kernel  1 block: refcount decrements of replaced pages, push the pages that
+//                    reached zero in ascending id order, empty the write pages, counters.
+#include "device_util.h"
+#include "gp_internal.h"
+
+namespace gp {
+namespace {
+
+enum { RQ_E = 0, RQ_NEED = 1, RQ_BASE = 2, RQ_STATE = 3, RQ_TOP = 4, RQ_N = 8 };
+enum { ST_NONE = 0, ST_PENDING = 1, ST_GO = 2, ST_DEFERRED = 3 };
+
+struct CompactArgs {
+  Geo g;
+  gp_pages pg;
+  ScratchPtrs sp;
+  const uint8_t* decision;
+  int32_t n_local;
+  int32_t* evicted_out;
+  int32_t* status_out;
+  int32_t* counters_out;
+};
+
+__device__ __forceinline__ void unit_of_block(const Geo& g, const ScratchPtrs& sp, int blk, int& b,
+                                              int& l, int& kvh) {
+  const int upr = g.L * g.Hkv;
+  const int rank = blk / upr;
+  const int rem = blk - rank * upr;
+  l = rem / g.Hkv;
+  kvh = rem - l * g.Hkv;
+  b = sp.order[rank];
+}
+
+__device__ __forceinline__ bool is_compacting(const CompactArgs& a, int b, int r) {
+  return a.sp.flags[b] == 0 && a.decision[b] == GP_DECISION_COMPACT && a.g.fill[r] == a.g.P;
+}
+
+// ----------------------------------------------------------------------------- keep-set
+__global__ __launch_bounds__(256) void keep_kernel(CompactArgs a) {
+  const Geo& g = a.g;
+  __shared__ int tmp[4];
+  __shared__ uint32_t cnt[256];
+  __shared__ uint32_t s_prefix, s_mask, s_below;
+  __shared__ int s_eqc, s_outc;
+  __shared__ float s_M[kDists], s_iz[kDists];
+  const int tid = threadIdx.x;
+  int b, l, kvh;
+  unit_of_block(g, a.sp, blockIdx.x, b, l, kvh);
+  const int64_t u = ((int64_t)b * g.L + l) * g.Hkv + kvh;
+  const int r = g.req_ids[b];
+  const int P = g.P;
+  if (!is_compacting(a, b, r)) {
+    if (a.evicted_out)
+      for (int i = tid; i < P; i += 256) a.evicted_out[u * P + i] = -1;
+    if (tid == 0) a.sp.e_unit[u] = 0x7fffffff;
+    return;
+  }
+  const int n = a.sp.n_tok[b];
+  const int k = g.n_alloc[r] * P;
+  const int E = n - k;
+  const int nl = min(max(a.n_local, 0), k);
+  const int cand = n - nl;
+  if (tid < kDists) {
+    const int h = kvh * kGroup + (tid >> 1);
+    const int64_t si = ((((int64_t)b * g.L + l) * g.Hq + h) * 2 + (tid & 1)) * 2;
+    s_M[tid] = a.sp.stats[si];
+    s_iz[tid] = 1.0f / a.sp.stats[si + 1];
+  }
+  __syncthreads();
+  const int64_t unit_base = (a.sp.tok_off[b] * g.L * g.Hkv + (int64_t)(l * g.Hkv + kvh) * n);
+  const float* x = a.sp.logits + unit_base * kDists;
+  float* imp = a.sp.imp + unit_base;
+  for (int i = tid; i < cand; i += 256) {
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < kDists; ++q)
+      v = fmaxf(v, exp2f((x[(int64_t)q * n + i] - s_M[q]) * kLog2e) * s_iz[q]);
+    imp[i] = v;
+  }
+  if (tid == 0) {
+    s_prefix = 0;
+    s_mask = 0;
+    s_below = 0;
+    s_eqc = 0;
+    s_outc = 0;
+  }
+  __syncthreads();
+  if (E > 0) {
+    // E-th smallest importance key (importance >= 0, so its float bits are ordered).
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      cnt[tid] = 0;
+      __syncthreads();
+      const uint32_t prefix = s_prefix, mask = s_mask;
+      for (int i = tid; i < cand; i += 256) {
+        const uint32_t key = __float_as_uint(imp[i]);
+        if ((key & mask) == prefix) atomicAdd(&cnt[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t acc = s_below, chosen = 255;
+        for (int bin = 0; bin < 256; ++bin) {
+          if (acc + cnt[bin] >= (uint32_t)E) {
+            chosen = (uint32_t)bin;
+            break;
+          }
+          acc += cnt[bin];
+        }
+        s_below = acc;
+        s_prefix = prefix | (chosen << shift);
+        s_mask = mask | (255u << shift);
+      }
+      __syncthreads();
+    }
+    const uint32_t kstar = s_prefix;
+    const int need = E - (int)s_below;
+    for (int base = 0; base < cand; base += 256) {
+      const int i = base + tid;
+      const uint32_t key = i < cand ? __float_as_uint(imp[i]) : 0xffffffffu;
+      const int lt = (i < cand && key < kstar) ? 1 : 0;
+      const int eq = (i < cand && key == kstar) ? 1 : 0;
+      int eqtot = 0, ftot = 0;
+      const int eqr = s_eqc + block_exscan_256(eq, tmp, &eqtot);
+      const int flag = (lt || (eq && eqr < need)) ? 1 : 0;
+      const int pos = s_outc + block_exscan_256(flag, tmp, &ftot);
+      if (flag && pos < E) {
+        a.sp.ev[u * P + pos] = i;
+        if (a.evicted_out) a.evicted_out[u * P + pos] = i;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        s_eqc += eqtot;
+        s_outc += ftot;
+      }
+      __syncthreads();
+    }
+  }
+  if (a.evicted_out)
+    for (int i = E + tid; i < P; i += 256) a.evicted_out[u * P + i] = -1;
+  __syncthreads();
+  if (tid == 0) a.sp.e_unit[u] = E > 0 ? a.sp.ev[u * P] : n;
+}
+
+// ----------------------------------------------------------------------------- per entry
+__global__ __launch_bounds__(256) void req_kernel(CompactArgs a) {
+  const Geo& g = a.g;
+  __shared__ int red[4];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int r = g.req_ids[b];
+  int32_t* rq = a.sp.req + (int64_t)b * RQ_N;
+  if (!is_compacting(a, b, r)) {
+    if (tid < RQ_N) rq[tid] = 0;
+    return;
+  }
+  const int upr = g.L * g.Hkv;
+  int e = 0x7fffffff;
+  for (int i = tid; i < upr; i += 256) e = min(e, a.sp.e_unit[(int64_t)b * upr + i]);
+  e = wave_min_int(e);
+  if ((tid & 63) == 0) red[tid >> 6] = e;
+  __syncthreads();
+  e = min(min(red[0], red[1]), min(red[2], red[3]));
+  __syncthreads();
+  const int A = g.n_alloc[r];
+  const int32_t* pt = g.page_table + (int64_t)r * g.max_pages;
+  int c = 0;
+  for (int j = e / g.P + tid; j < A; j += 256) c += a.pg.refcount[pt[j]] > 1 ? 1 : 0;
+  c = wave_sum_int(c);
+  if ((tid & 63) == 0) red[tid >> 6] = c;
+  __syncthreads();
+  if (tid == 0) {
+    rq[RQ_E] = e;
+    rq[RQ_NEED] = red[0] + red[1] + red[2] + red[3];
+    rq[RQ_BASE] = 0;
+    rq[RQ_STATE] = ST_PENDING;
+    rq[RQ_TOP] = 0;
+  }
+}
+
+// ----------------------------------------------------------------------------- plan
+constexpr int kPlanChunk = 2048;
+
+__global__ __launch_bounds__(1024) void cowplan_kernel(CompactArgs a) {
+  __shared__ int c_need[kPlanChunk], c_state[kPlanChunk], c_base[kPlanChunk], c_top[kPlanChunk];
+  __shared__ int s_top, s_cum;
+  const int tid = threadIdx.x;
+  const int n_req = a.g.n_req;
+  if (tid == 0) {
+    s_top = *a.pg.free_top;
+    s_cum = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < n_req; base += kPlanChunk) {
+    const int cnt = min(kPlanChunk, n_req - base);
+    for (int i = tid; i < cnt; i += 1024) {
+      const int32_t* rq = a.sp.req + (int64_t)(base + i) * RQ_N;
+      c_need[i] = rq[RQ_NEED];
+      c_state[i] = rq[RQ_STATE];
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int top = s_top, cum = s_cum;
+      for (int i = 0; i < cnt; ++i) {
+        if (c_state[i] != ST_PENDING) continue;
+        if (c_need[i] <= top) {
+          c_top[i] = top;
+          c_base[i] = cum;
+          top -= c_need[i];
+          cum += c_need[i];
+          c_state[i] = ST_GO;
+        } else {
+          c_state[i] = ST_DEFERRED;
+        }
+      }
+      s_top = top;
+      s_cum = cum;
+    }
+    __syncthreads();
+    for (int i = tid; i < cnt; i += 1024) {
+      int32_t* rq = a.sp.req + (int64_t)(base + i) * RQ_N;
+      rq[RQ_STATE] = c_state[i];
+      if (c_state[i] == ST_GO) {
+        rq[RQ_BASE] = c_base[i];
+        rq[RQ_TOP] = c_top[i];
+      }
+      if (c_state[i] == ST_DEFERRED) a.status_out[base + i] |= GP_REQ_DEFERRED;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    *a.pg.free_top = s_top;
+    a.sp.misc[0] = s_cum;
+  }
+}
+
+__global__ __launch_bounds__(256) void cowassign_kernel(CompactArgs a) {
+  const Geo& g = a.g;
+  __shared__ int tmp[4];
+  __shared__ int s_carry;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int32_t* rq = a.sp.req + (int64_t)b * RQ_N;
+  if (rq[RQ_STATE] != ST_GO || rq[RQ_NEED] == 0) return;
+  const int r = g.req_ids[b];
+  const int A = g.n_alloc[r];
+  const int j0 = rq[RQ_E] / g.P;
+  const int cbase = rq[RQ_BASE];
+  const int ptop = rq[RQ_TOP];
+  int32_t* pt = a.pg.page_table + (int64_t)r * g.max_pages;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (int jb = j0; jb < A; jb += 256) {
+    const int j = jb + tid;
+    int old = -1;
+    int flag = 0;
+    if (j < A) {
+      old = pt[j];
+      flag = a.pg.refcount[old] > 1 ? 1 : 0;
+    }
+    int total = 0;
+    const int idx = s_carry + block_exscan_256(flag, tmp, &total);
+    if (flag) {
+      const int fresh = a.pg.free_stack[ptop - 1 - idx];
+      a.sp.cow[(int64_t)(cbase + idx) * 2] = old;
+      a.sp.cow[(int64_t)(cbase + idx) * 2 + 1] = fresh;
+      pt[j] = fresh;
+      a.pg.refcount[fresh] = 1;
+    }
+    __syncthreads();
+    if (tid == 0) s_carry += total;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void cowcopy_kernel(CompactArgs a) {
+  const Geo& g = a.g;
+  const int tid = threadIdx.x;
+  const int ncow = a.sp.misc[0];
+  const int per = g.L * g.Hkv * 2;
+  const long long items = (long long)ncow * per;
+  const int esz = g.dtype == GP_BF16 ? 2 : 4;
+  const int cpr = g.d * esz / 16;  // 16-byte chunks per row
+  const int rpp = 256 / cpr;       // rows per pass
+  for (long long it = blockIdx.x; it < items; it += gridDim.x) {
+    const int e = (int)(it / per);
+    const int rem = (int)(it - (long long)e * per);
+    const int which = rem & 1;
+    const int lg = rem >> 1;
+    const int l = lg / g.Hkv;
+    const int kvh = lg - l * g.Hkv;
+    const int old = a.sp.cow[(int64_t)e * 2];
+    const int fresh = a.sp.cow[(int64_t)e * 2 + 1];
+    char* base = reinterpret_cast<char*>(const_cast<void*>(which ? g.v : g.k));
+    const int64_t hoff = (int64_t)l * g.s_layer + (int64_t)kvh * g.s_head;
+    const char* src = base + (hoff + (int64_t)old * g.s_page) * esz;
+    char* dst = base + (hoff + (int64_t)fresh * g.s_page) * esz;
+    const int c = tid % cpr;
+    for (int row = tid / cpr; row < g.P; row += rpp) {
+      const int64_t ro = (int64_t)row * g.s_tok * esz + (int64_t)c * 16;
+      *reinterpret_cast<uint4*>(dst + ro) = *reinterpret_cast<const uint4*>(src + ro);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- gather
+template <int NV>  // 16-byte vectors per thread per row part (a row is 4 parts)
+__global__ __launch_bounds__(256) void gather_kernel(CompactArgs a) {
+  const Geo& g = a.g;
+  __shared__ int s_ev[256];
+  const int tid = threadIdx.x;
+  int b, l, kvh;
+  unit_of_block(g, a.sp, blockIdx.x, b, l, kvh);
+  const int32_t* rq = a.sp.req + (int64_t)b * RQ_N;
+  if (rq[RQ_STATE] != ST_GO) return;
+  const int r = g.req_ids[b];
+  const int P = g.P;
+  const int n = a.sp.n_tok[b];
+  const int k = g.n_alloc[r] * P;
+  const int E = n - k;
+  const int64_t u = ((int64_t)b * g.L + l) * g.Hkv + kvh;
+  const int e = a.sp.e_unit[u];
+  if (e >= k) return;
+  for (int i = tid; i < E; i += 256) s_ev[i] = a.sp.ev[u * P + i];
+  __syncthreads();
+  const int esz = g.dtype == GP_BF16 ? 2 : 4;
+  const int32_t* pt = a.pg.page_table + (int64_t)r * g.max_pages;
+  const int64_t hoff = ((int64_t)l * g.s_layer + (int64_t)kvh * g.s_head) * esz;
+  char* kb = reinterpret_cast<char*>(const_cast<void*>(g.k)) + hoff;
+  char* vb = reinterpret_cast<char*>(const_cast<void*>(g.v)) + hoff;
+  const int part = tid & 3;
+  const int rr = tid >> 2;
+  const int64_t pbytes = (int64_t)NV * 16;
+  for (int j0 = e; j0 < k; j0 += 64) {
+    const int jj = j0 + rr;
+    const bool act = jj < k;
+    uint4 kv[NV], vv[NV];
+    int64_t dsto = 0;
+    if (act) {
+      int s = 0;
+      for (int m = 0; m < E; ++m) s += (s_ev[m] <= jj + s) ? 1 : 0;
+      const int src = jj + s;
+      const int64_t srco = ((int64_t)pt[src / P] * g.s_page + (int64_t)(src % P) * g.s_tok) * esz + part * pbytes;
+      dsto = ((int64_t)pt[jj / P] * g.s_page + (int64_t)(jj % P) * g.s_tok) * esz + part * pbytes;
+#pragma unroll
+      for (int q = 0; q < NV; ++q) {
+        kv[q] = *reinterpret_cast<const uint4*>(kb + srco + q * 16);
+        vv[q] = *reinterpret_cast<const uint4*>(vb + srco + q * 16);
+      }
+    }
+    __syncthreads();
+    if (act) {
+#pragma unroll
+      for (int q = 0; q < NV; ++q) {
+        *reinterpret_cast<uint4*>(kb + dsto + q * 16) = kv[q];
+        *reinterpret_cast<uint4*>(vb + dsto + q * 16) = vv[q];
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- finalize
+__global__ __launch_bounds__(1024) void finalize_kernel(CompactArgs a) {
+  const Geo& g = a.g;
+  __shared__ int tmp[16];
+  __shared__ int s_carry;
+  __shared__ unsigned long long s_moved;
+  __shared__ int s_comp, s_def;
+  const int tid = threadIdx.x;
+  const int ncow = a.sp.misc[0];
+  const int words = g.num_pages / 32 + 1;
+  for (int w = tid; w < words; w += 1024) a.sp.bitmap[w] = 0u;
+  if (tid == 0) {
+    s_carry = 0;
+    s_moved = 0;
+    s_comp = 0;
+    s_def = 0;
+  }
+  __syncthreads();
+  for (int e = tid; e < ncow; e += 1024) {
+    const int old = a.sp.cow[(int64_t)e * 2];
+    if (atomicSub(&a.pg.refcount[old], 1) == 1) atomicOr(&a.sp.bitmap[old >> 5], 1u << (old & 31));
+  }
+  __threadfence();
+  __syncthreads();
+  const int top = *a.pg.free_top;
+  for (int wb = 0; wb < words; wb += 1024) {
+    const int w = wb + tid;
+    const uint32_t bits = w < words ? a.sp.bitmap[w] : 0u;
+    int total = 0;
+    int pos = s_carry + block_exscan_1024(__popc(bits), tmp, &total);
+    for (int bit = 0; bit < 32; ++bit)
+      if (bits & (1u << bit)) a.pg.free_stack[top + pos++] = w * 32 + bit;
+    __syncthreads();
+    if (tid == 0) s_carry += total;
+    __syncthreads();
+  }
+  // Empty the write pages of compacted entries; counters.
+  for (int b = tid; b < g.n_req; b += 1024) {
+    const int st = a.sp.req[(int64_t)b * RQ_N + RQ_STATE];
+    if (st == ST_GO) {
+      a.pg.fill[g.req_ids[b]] = 0;
+      atomicAdd(&s_comp, 1);
+    } else if (st == ST_DEFERRED) {
+      atomicAdd(&s_def, 1);
+    }
+  }
+  const int upr = g.L * g.Hkv;
+  unsigned long long moved = 0;
+  for (long long uu = tid; uu < (long long)g.n_req * upr; uu += 1024) {
+    const int b = (int)(uu / upr);
+    if (a.sp.req[(int64_t)b * RQ_N + RQ_STATE] != ST_GO) continue;
+    const int k = g.n_alloc[g.req_ids[b]] * g.P;
+    const int e = a.sp.e_unit[uu];
+    if (e < k) moved += (unsigned long long)(k - e);
+  }
+  atomicAdd(&s_moved, moved);
+  __syncthreads();
+  if (tid == 0) {
+    *a.pg.free_top = top + s_carry;
+    if (a.counters_out) {
+      a.counters_out[GP_CNT_COMPACTS] = s_comp;
+      a.counters_out[GP_CNT_DEFERRED] = s_def;
+      a.counters_out[GP_CNT_COW_PAGES] = ncow;
+      a.counters_out[GP_CNT_FREED_PAGES] = s_carry;
+      a.counters_out[GP_CNT_MOVED_ROWS] = (int32_t)min(s_moved, (unsigned long long)INT32_MAX);
+      a.counters_out[GP_CNT_COPIED_ROWS] = (int32_t)min((long long)ncow * upr * g.P, (long long)INT32_MAX);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- append
+__global__ __launch_bounds__(256) void append_write_kernel(Geo g, gp_pages pg, const void* k_new,
+                                                           const void* v_new) {
+  const int b = blockIdx.x / g.L;
+  const int l = blockIdx.x - b * g.L;
+  const int r = g.req_ids[b];
+  const int f = pg.fill[r];
+  if (f >= g.P) return;
+  const int page = pg.page_table[(int64_t)r * pg.max_pages + pg.n_alloc[r]];
+  const int esz = g.dtype == GP_BF16 ? 2 : 4;
+  const int cpr = g.d * esz / 16;
+  const int items = g.Hkv * cpr * 2;
+  for (int it = threadIdx.x; it < items; it += 256) {
+    const int which = it / (g.Hkv * cpr);
+    const int rem = it - which * g.Hkv * cpr;
+    const int kvh = rem / cpr;
+    const int c = rem - kvh * cpr;
+    const char* src = reinterpret_cast<const char*>(which ? v_new : k_new) +
+                      ((((int64_t)b * g.L + l) * g.Hkv + kvh) * g.d) * esz + c * 16;
+    char* dst = reinterpret_cast<char*>(const_cast<void*>(which ? g.v : g.k)) +
+                ((int64_t)l * g.s_layer + (int64_t)page * g.s_page + (int64_t)kvh * g.s_head +
+                 (int64_t)f * g.s_tok) * esz + c * 16;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  }
+}
+
+__global__ __launch_bounds__(256) void append_bump_kernel(Geo g, gp_pages pg, int32_t* status) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= g.n_req) return;
+  const int r = g.req_ids[b];
+  if (pg.fill[r] < g.P) {
+    pg.fill[r] += 1;
+  } else if (status) {
+    status[b] |= GP_REQ_OVERFLOW;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_compact(const Geo& g, const gp_pages& pg, const ScratchPtrs& sp,
+                          const uint8_t* decision, int32_t n_local, int32_t* evicted_out,
+                          int32_t* status_out, int32_t* counters_out, hipStream_t st) {
+  CompactArgs a{g, pg, sp, decision, n_local, evicted_out, status_out, counters_out};
+  const unsigned units = (unsigned)((int64_t)g.n_req * g.L * g.Hkv);
+  hipLaunchKernelGGL(keep_kernel, dim3(units), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(req_kernel, dim3((unsigned)g.n_req), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(cowplan_kernel, dim3(1), dim3(1024), 0, st, a);
+  hipLaunchKernelGGL(cowassign_kernel, dim3((unsigned)g.n_req), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(cowcopy_kernel, dim3(2048), dim3(256), 0, st, a);
+  const int esz = g.dtype == GP_BF16 ? 2 : 4;
+  const int nv = g.d * esz / 64;  // 16-byte vectors per quarter row
+  if (nv == 2)
+    hipLaunchKernelGGL(gather_kernel<2>, dim3(units), dim3(256), 0, st, a);
+  else if (nv == 4)
+    hipLaunchKernelGGL(gather_kernel<4>, dim3(units), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(gather_kernel<8>, dim3(units), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const Geo& g, const gp_pages& pg, const void* k_new, const void* v_new,
+                         int32_t* status_out, hipStream_t st) {
+  hipLaunchKernelGGL(append_write_kernel, dim3((unsigned)(g.n_req * g.L)), dim3(256), 0, st, g, pg,
+                     k_new, v_new);
+  hipLaunchKernelGGL(append_bump_kernel, dim3((unsigned)((g.n_req + 255) / 256)), dim3(256), 0, st,
+                     g, pg, status_out);
+  return hipGetLastError();
+}
+
+}  // namespace gp

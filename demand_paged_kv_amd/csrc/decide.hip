@@ -1,0 +1,109 @@
+// Boundary decision and grow (GrowPage review on evolve.pub, "Summary": a larger recent
+// working set triggers allocation of one extra physical page, otherwise compact; FAQ
+// "Is GrowPage's code available?": demand threshold tau 0).
+//
+// delta_b = sum over layers and query heads of (W_short - W_long); grow iff delta > tau.
+// Grows pop the device free stack in batch order: the eligible entries are ranked by a
+// block prefix sum and the first `free_top` of them receive free_stack[top-1-rank], so
+// page ids are deterministic without atomics.  One 1024-thread block: the batch is
+// small and the work is latency-bound integer bookkeeping.
+#include "device_util.h"
+#include "gp_internal.h"
+
+namespace gp {
+namespace {
+
+struct DecideArgs {
+  const int32_t* ws;
+  const int32_t* req_ids;
+  int32_t n_req, L, Hq, tau, P;
+  gp_pages pg;
+  uint8_t* decision;
+  int32_t* delta;
+  int32_t* status;
+  int32_t* counters;
+};
+
+__global__ __launch_bounds__(1024) void decide_kernel(DecideArgs a) {
+  __shared__ int tmp[16];
+  __shared__ int s_carry, s_top0, s_denied;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int per = a.L * a.Hq;
+
+  // Delta per entry, one wave per entry (coalesced reads of the working sets).
+  for (int b = wave; b < a.n_req; b += 16) {
+    const int32_t* w = a.ws + (int64_t)b * per * 2;
+    long long acc = 0;
+    for (int i = lane; i < per; i += 64) acc += (long long)w[2 * i] - w[2 * i + 1];
+    acc = wave_sum_i64(acc);
+    if (lane == 0) {
+      const long long c = acc > INT32_MAX ? INT32_MAX : (acc < INT32_MIN ? INT32_MIN : acc);
+      a.delta[b] = (int32_t)c;
+    }
+  }
+  if (tid == 0) {
+    s_carry = 0;
+    s_top0 = *a.pg.free_top;
+    s_denied = 0;
+  }
+  __syncthreads();
+  const int top0 = s_top0;
+  for (int base = 0; base < a.n_req; base += 1024) {
+    const int b = base + tid;
+    int eligible = 0, want = 0, st = 0, r = 0, A = 0;
+    if (b < a.n_req) {
+      r = a.req_ids[b];
+      A = a.pg.n_alloc[r];
+      const bool over = a.ws[(int64_t)b * per * 2] < 0;
+      const bool at = a.pg.fill[r] == a.P;
+      if (over) st |= GP_REQ_OVERFLOW;
+      if (!at) st |= GP_REQ_NOT_AT_BOUNDARY;
+      want = (!over && at && a.delta[b] > a.tau) ? 1 : 0;
+      eligible = (want && A + 2 <= a.pg.max_pages) ? 1 : 0;
+    }
+    int total = 0;
+    const int rk = s_carry + block_exscan_1024(eligible, tmp, &total);
+    if (b < a.n_req) {
+      const bool granted = eligible && rk < top0;
+      if (want && !granted) {
+        st |= GP_REQ_GROW_DENIED;
+        atomicAdd(&s_denied, 1);
+      }
+      if (granted) {
+        const int page = a.pg.free_stack[top0 - 1 - rk];
+        a.pg.page_table[(int64_t)r * a.pg.max_pages + A + 1] = page;
+        a.pg.refcount[page] = 1;
+        a.pg.n_alloc[r] = A + 1;
+        a.pg.fill[r] = 0;
+      }
+      a.decision[b] = granted ? GP_DECISION_GROW : GP_DECISION_COMPACT;
+      a.status[b] = st;
+    }
+    __syncthreads();
+    if (tid == 0) s_carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const int grows = min(s_carry, top0);
+    *a.pg.free_top = top0 - grows;
+    if (a.counters) {
+      a.counters[GP_CNT_GROWS] = grows;
+      a.counters[GP_CNT_GROW_DENIED] = s_denied;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_req, int32_t L,
+                         int32_t Hq, int32_t tau, const gp_pages& pg, int32_t P,
+                         uint8_t* decision, int32_t* delta, int32_t* status, int32_t* counters,
+                         hipStream_t st) {
+  DecideArgs a{ws, req_ids, n_req, L, Hq, tau, P, pg, decision, delta, status, counters};
+  hipLaunchKernelGGL(decide_kernel, dim3(1), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace gp

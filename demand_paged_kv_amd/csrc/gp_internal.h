@@ -1,0 +1,145 @@
+// Internal declarations of libgrowpage: scratch layout, argument blocks and the
+// launchers each kernel file provides.  Device code targets gfx950 (wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "growpage.h"
+
+namespace gp {
+
+constexpr int kWave = 64;
+constexpr int kDists = 8;          // 4 query heads per KV head x 2 summaries
+constexpr int kGroup = 4;          // query heads per KV head
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kMassScale = 1099511627776.0f;  // 2^40: fixed-point softmax mass
+
+// ----------------------------------------------------------------------------- scratch
+// One caller buffer, carved into 256-byte aligned regions.  The scan fills the
+// request plan, logits and statistics; the compaction reads them.
+struct ScratchLayout {
+  size_t tok_off;   // int64 [n_req]  first candidate token of each entry
+  size_t n_tok;     // int32 [n_req]  candidate slots n (0 when over budget)
+  size_t order;     // int32 [n_req]  entries by n descending (ties by index)
+  size_t flags;     // int32 [n_req]  GP_REQ_OVERFLOW when over budget
+  size_t stats;     // float [n_req][L][Hq][2][2]  max logit, sum exp
+  size_t logits;    // float [tokens][L][Hkv][8] (per unit: [8][n])
+  size_t imp;       // float [tokens][L][Hkv]
+  size_t ev;        // int32 [n_req][L][Hkv][P]  evicted slots, ascending
+  size_t e_unit;    // int32 [n_req][L][Hkv]     first evicted slot (n if none)
+  size_t req;       // int32 [n_req][4]  e_req, cow_need, cow_base, go
+  size_t cow;       // int32 [cow_cap][2]  (old page, new page)
+  size_t misc;      // int32 [16]  ncow, ...
+  size_t bitmap;    // uint32 [num_pages/32 + 1]
+  size_t total;
+  int64_t cow_cap;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline ScratchLayout scratch_layout(const gp_kv& kv, int32_t n_req, int64_t max_tokens) {
+  ScratchLayout s{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const size_t nr = (size_t)(n_req > 0 ? n_req : 1);
+  const size_t units = nr * kv.L * kv.Hkv;
+  const size_t tok = (size_t)(max_tokens > 0 ? max_tokens : 1);
+  s.tok_off = take(nr * sizeof(int64_t));
+  s.n_tok = take(nr * sizeof(int32_t));
+  s.order = take(nr * sizeof(int32_t));
+  s.flags = take(nr * sizeof(int32_t));
+  s.stats = take(nr * kv.L * kv.Hq * 4 * sizeof(float));
+  s.logits = take(tok * kv.L * kv.Hkv * kDists * sizeof(float));
+  s.imp = take(tok * kv.L * kv.Hkv * sizeof(float));
+  s.ev = take(units * kv.P * sizeof(int32_t));
+  s.e_unit = take(units * sizeof(int32_t));
+  s.req = take(nr * 4 * sizeof(int32_t));
+  s.cow_cap = (int64_t)(tok / (kv.P > 0 ? kv.P : 1) + nr);
+  s.cow = take((size_t)s.cow_cap * 2 * sizeof(int32_t));
+  s.misc = take(16 * sizeof(int32_t));
+  s.bitmap = take(((size_t)kv.num_pages / 32 + 1) * sizeof(uint32_t));
+  s.total = off;
+  return s;
+}
+
+// Pointers into the scratch buffer, passed to kernels by value.
+struct ScratchPtrs {
+  int64_t* tok_off;
+  int32_t* n_tok;
+  int32_t* order;
+  int32_t* flags;
+  float* stats;
+  float* logits;
+  float* imp;
+  int32_t* ev;
+  int32_t* e_unit;
+  int32_t* req;
+  int32_t* cow;
+  int32_t* misc;
+  uint32_t* bitmap;
+  int64_t cow_cap;
+};
+
+inline ScratchPtrs scratch_ptrs(void* base, const ScratchLayout& s) {
+  char* b = (char*)base;
+  ScratchPtrs p;
+  p.tok_off = (int64_t*)(b + s.tok_off);
+  p.n_tok = (int32_t*)(b + s.n_tok);
+  p.order = (int32_t*)(b + s.order);
+  p.flags = (int32_t*)(b + s.flags);
+  p.stats = (float*)(b + s.stats);
+  p.logits = (float*)(b + s.logits);
+  p.imp = (float*)(b + s.imp);
+  p.ev = (int32_t*)(b + s.ev);
+  p.e_unit = (int32_t*)(b + s.e_unit);
+  p.req = (int32_t*)(b + s.req);
+  p.cow = (int32_t*)(b + s.cow);
+  p.misc = (int32_t*)(b + s.misc);
+  p.bitmap = (uint32_t*)(b + s.bitmap);
+  p.cow_cap = s.cow_cap;
+  return p;
+}
+
+// Geometry shared by the scan, selection and compaction kernels.
+struct Geo {
+  const void* k;
+  const void* v;
+  int64_t s_layer, s_page, s_head, s_tok;
+  int32_t L, Hq, Hkv, d, P, num_pages;
+  int32_t dtype;
+  const int32_t* page_table;
+  int32_t max_pages;
+  const int32_t* n_alloc;
+  const int32_t* fill;
+  const int32_t* req_ids;
+  int32_t n_req;
+};
+
+// ----------------------------------------------------------------------------- launchers
+hipError_t launch_ema(const void* q, int32_t q_dtype, int64_t sr, int64_t sl, int64_t sh,
+                      const int32_t* req_ids, int32_t n_req, int32_t L, int32_t Hq, int32_t d,
+                      float* sum_s, float* sum_l, float beta_s, float beta_l, hipStream_t st);
+
+hipError_t launch_scan(const Geo& g, const ScratchPtrs& sp, int64_t max_tokens,
+                       const float* sum_s, const float* sum_l, const float* rope_cos,
+                       const float* rope_sin, int32_t rope_max_pos, const int32_t* pos,
+                       float top_p, int32_t* ws_out, float* stats_out, hipStream_t st);
+
+hipError_t launch_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_req, int32_t L,
+                         int32_t Hq, int32_t tau, const gp_pages& pg, int32_t P,
+                         uint8_t* decision, int32_t* delta, int32_t* status, int32_t* counters,
+                         hipStream_t st);
+
+hipError_t launch_compact(const Geo& g, const gp_pages& pg, const ScratchPtrs& sp,
+                          const uint8_t* decision, int32_t n_local, int32_t* evicted_out,
+                          int32_t* status_out, int32_t* counters_out, hipStream_t st);
+
+hipError_t launch_append(const Geo& g, const gp_pages& pg, const void* k_new, const void* v_new,
+                         int32_t* status_out, hipStream_t st);
+
+}  // namespace gp

@@ -1,0 +1,434 @@
+// Boundary scan: logits of both summaries against every retained key, per-head softmax
+// statistics and the Top-p attention working-set size of each summary.
+// (GrowPage review on evolve.pub, "Summary": compare the Top-p attention working-set
+// sizes induced by the short- and long-timescale summaries, kept pre-RoPE.)
+//
+// Three launches:
+//   plan_kernel    1 block: candidate slots n of every batch entry, token offsets into
+//                  the scratch, and a longest-first order of the entries.
+//   logit_kernel   one wave per (entry, layer, KV head) "unit", launched longest-first.
+//                  The wave streams the unit's K rows through the page table once;
+//                  8 lanes share a token row (each holds 2 x D/16 elements), every lane
+//                  keeps the matching slices of all 8 rotated summaries (4 query heads x
+//                  2 timescales) in registers, and a 3-step DPP transpose-reduce leaves
+//                  lane j with the logit of summary j for its token.  Logits go to the
+//                  scratch ([unit][8][n] float32), the running max to the statistics.
+//   select_kernel  one 256-thread block per (unit, summary): exact radix select on the
+//                  ordered float key of the logits (4 passes of 8 bits), weighted by the
+//                  softmax mass exp(l - M) in 2^-40 fixed point (order-independent sums),
+//                  gives the smallest m whose m largest probabilities reach top_p.
+#include "device_util.h"
+#include "gp_internal.h"
+
+namespace gp {
+namespace {
+
+struct ScanArgs {
+  Geo g;
+  ScratchPtrs sp;
+  int64_t max_tokens;
+  const float* sum_s;
+  const float* sum_l;
+  const float* rope_cos;
+  const float* rope_sin;
+  int32_t rope_max_pos;
+  const int32_t* pos;
+  float scale;
+  float top_p;
+  int32_t* ws_out;
+  float* stats_out;
+};
+
+// ----------------------------------------------------------------------------- plan
+constexpr int kPlanLds = 8192;
+
+__global__ __launch_bounds__(1024) void plan_kernel(ScanArgs a) {
+  __shared__ int tmp[16];
+  __shared__ long long carry_s;
+  __shared__ int nvals[kPlanLds];
+  const int tid = threadIdx.x;
+  const Geo& g = a.g;
+  if (tid == 0) carry_s = 0;
+  __syncthreads();
+  for (int base = 0; base < g.n_req; base += 1024) {
+    const int b = base + tid;
+    int n = 0;
+    if (b < g.n_req) {
+      const int r = g.req_ids[b];
+      n = g.n_alloc[r] * g.P + g.fill[r];
+    }
+    int total = 0;
+    const int ex = block_exscan_1024(n, tmp, &total);  // fits int: per chunk < 2^31 tokens
+    const long long off = carry_s + ex;
+    if (b < g.n_req) {
+      const bool over = off + n > a.max_tokens;
+      a.sp.tok_off[b] = over ? 0 : off;
+      a.sp.n_tok[b] = over ? 0 : n;
+      a.sp.flags[b] = over ? GP_REQ_OVERFLOW : 0;
+      if (b < kPlanLds) nvals[b] = over ? -1 : n;
+    }
+    __syncthreads();
+    if (tid == 0) carry_s += total;
+    __syncthreads();
+  }
+  // Longest-first order (rank sort, ties by batch index) so long units start first.
+  if (g.n_req <= kPlanLds) {
+    for (int b = tid; b < g.n_req; b += 1024) {
+      const int nb = nvals[b];
+      int rank = 0;
+      for (int c = 0; c < g.n_req; ++c) {
+        const int nc = nvals[c];
+        rank += (nc > nb) || (nc == nb && c < b);
+      }
+      a.sp.order[rank] = b;
+    }
+  } else {
+    for (int b = tid; b < g.n_req; b += 1024) a.sp.order[b] = b;
+  }
+}
+
+// ----------------------------------------------------------------------------- logits
+template <bool BF16, int D>
+struct Chunk;  // 2 x (D/16) elements of one row, as raw bits
+
+template <>
+struct Chunk<true, 128> {  // 2 x 8 bf16 = 2 x 16 B
+  uint4 c0, c1;
+};
+template <>
+struct Chunk<true, 64> {  // 2 x 4 bf16 = 2 x 8 B
+  uint2 c0, c1;
+};
+template <>
+struct Chunk<false, 64> {  // 2 x 4 f32 = 2 x 16 B
+  uint4 c0, c1;
+};
+template <>
+struct Chunk<false, 128> {  // 2 x 8 f32 = 2 x 32 B
+  uint4 c0, c0b, c1, c1b;
+};
+
+template <bool BF16, int D>
+__device__ __forceinline__ void load_chunk(Chunk<BF16, D>& c, const char* row, int j) {
+  constexpr int W = D / 16;
+  constexpr int E = BF16 ? 2 : 4;
+  const char* p0 = row + (size_t)j * W * E;
+  const char* p1 = row + (size_t)(D / 2 + j * W) * E;
+  if constexpr (BF16 && D == 128) {
+    c.c0 = *reinterpret_cast<const uint4*>(p0);
+    c.c1 = *reinterpret_cast<const uint4*>(p1);
+  } else if constexpr (BF16 && D == 64) {
+    c.c0 = *reinterpret_cast<const uint2*>(p0);
+    c.c1 = *reinterpret_cast<const uint2*>(p1);
+  } else if constexpr (!BF16 && D == 64) {
+    c.c0 = *reinterpret_cast<const uint4*>(p0);
+    c.c1 = *reinterpret_cast<const uint4*>(p1);
+  } else {
+    c.c0 = *reinterpret_cast<const uint4*>(p0);
+    c.c0b = *reinterpret_cast<const uint4*>(p0 + 16);
+    c.c1 = *reinterpret_cast<const uint4*>(p1);
+    c.c1b = *reinterpret_cast<const uint4*>(p1 + 16);
+  }
+}
+
+__device__ __forceinline__ void unpack_bf16x2(uint32_t w, float& lo, float& hi) {
+  lo = __uint_as_float(w << 16);
+  hi = __uint_as_float(w & 0xffff0000u);
+}
+
+template <bool BF16, int D>
+__device__ __forceinline__ void unpack_chunk(const Chunk<BF16, D>& c, float* kf) {
+  constexpr int W = D / 16;
+  if constexpr (BF16 && D == 128) {
+    const uint32_t a[4] = {c.c0.x, c.c0.y, c.c0.z, c.c0.w};
+    const uint32_t b[4] = {c.c1.x, c.c1.y, c.c1.z, c.c1.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      unpack_bf16x2(a[i], kf[2 * i], kf[2 * i + 1]);
+      unpack_bf16x2(b[i], kf[W + 2 * i], kf[W + 2 * i + 1]);
+    }
+  } else if constexpr (BF16 && D == 64) {
+    unpack_bf16x2(c.c0.x, kf[0], kf[1]);
+    unpack_bf16x2(c.c0.y, kf[2], kf[3]);
+    unpack_bf16x2(c.c1.x, kf[W + 0], kf[W + 1]);
+    unpack_bf16x2(c.c1.y, kf[W + 2], kf[W + 3]);
+  } else if constexpr (!BF16 && D == 64) {
+    kf[0] = __uint_as_float(c.c0.x);
+    kf[1] = __uint_as_float(c.c0.y);
+    kf[2] = __uint_as_float(c.c0.z);
+    kf[3] = __uint_as_float(c.c0.w);
+    kf[W + 0] = __uint_as_float(c.c1.x);
+    kf[W + 1] = __uint_as_float(c.c1.y);
+    kf[W + 2] = __uint_as_float(c.c1.z);
+    kf[W + 3] = __uint_as_float(c.c1.w);
+  } else {
+    const uint32_t a[8] = {c.c0.x, c.c0.y, c.c0.z, c.c0.w, c.c0b.x, c.c0b.y, c.c0b.z, c.c0b.w};
+    const uint32_t b[8] = {c.c1.x, c.c1.y, c.c1.z, c.c1.w, c.c1b.x, c.c1b.y, c.c1b.z, c.c1b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      kf[i] = __uint_as_float(a[i]);
+      kf[W + i] = __uint_as_float(b[i]);
+    }
+  }
+}
+
+// Summary index held in register slot i by lane j of a token group: slots 0..3 hold
+// j^i and slots 4..7 hold j^7^i, so that the reduce steps (pairs j<->j^7 by half-row
+// mirror, then j<->j^2, then j<->j^1) always add a partner's slot holding the same
+// summary and lane j finishes with summary j.
+__device__ __forceinline__ int slot_dist(int j, int i) { return i < 4 ? (j ^ i) : (j ^ 7 ^ (i - 4)); }
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(64) void logit_kernel(ScanArgs a) {
+#pragma clang fp contract(off)
+  constexpr int W = D / 16;
+  constexpr int U = 4;  // token steps per load batch
+  constexpr int E = BF16 ? 2 : 4;
+  const Geo& g = a.g;
+  const int lane = threadIdx.x;
+  const int tl = lane >> 3;
+  const int j = lane & 7;
+  const int upr = g.L * g.Hkv;
+  const int rank = blockIdx.x / upr;
+  const int rem = blockIdx.x - rank * upr;
+  const int l = rem / g.Hkv;
+  const int kvh = rem - l * g.Hkv;
+  const int b = a.sp.order[rank];
+  if (a.sp.flags[b]) return;
+  const int n = a.sp.n_tok[b];
+  const int r = g.req_ids[b];
+
+  // Rotate the 8 summaries to the request position and fold in 1/sqrt(d).
+  float qr[8][2 * W];
+  const bool rope = a.rope_cos != nullptr;
+  int pos = 0;
+  if (rope) pos = min(max(a.pos[r], 0), a.rope_max_pos - 1);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int dist = slot_dist(j, i);
+    const float* s = ((dist & 1) ? a.sum_l : a.sum_s) +
+                     (((int64_t)r * g.L + l) * g.Hq + kvh * kGroup + (dist >> 1)) * D;
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+      const float x1 = s[j * W + e];
+      const float x2 = s[D / 2 + j * W + e];
+      if (rope) {
+        const float c = a.rope_cos[(int64_t)pos * (D / 2) + j * W + e];
+        const float sn = a.rope_sin[(int64_t)pos * (D / 2) + j * W + e];
+        qr[i][e] = (x1 * c - x2 * sn) * a.scale;
+        qr[i][W + e] = (x2 * c + x1 * sn) * a.scale;
+      } else {
+        qr[i][e] = x1 * a.scale;
+        qr[i][W + e] = x2 * a.scale;
+      }
+    }
+  }
+
+  const int64_t unit_base =
+      (a.sp.tok_off[b] * g.L * g.Hkv + (int64_t)(l * g.Hkv + kvh) * n) * kDists;
+  float* lg = a.sp.logits + unit_base + (int64_t)j * n;
+  const char* kb = reinterpret_cast<const char*>(g.k) + ((int64_t)l * g.s_layer + (int64_t)kvh * g.s_head) * E;
+  const int32_t* pt = g.page_table + (int64_t)r * g.max_pages;
+  float m = -INFINITY;
+
+  for (int t0 = 0; t0 < n; t0 += 8 * U) {
+    Chunk<BF16, D> raw[U] = {};
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ts = t0 + u * 8;
+      if (ts < n) {
+        const int page = pt[ts / g.P];
+        const int slot = (ts % g.P) + tl;
+        const char* row = kb + ((int64_t)page * g.s_page + (int64_t)slot * g.s_tok) * E;
+        if (ts + tl < n) load_chunk<BF16, D>(raw[u], row, j);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ts = t0 + u * 8;
+      if (ts >= n) break;
+      float kf[2 * W];
+      unpack_chunk<BF16, D>(raw[u], kf);
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 2 * W; ++e) s = __builtin_fmaf(qr[i][e], kf[e], s);
+        acc[i] = s;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += dpp_mov<kDppHalfMirror>(acc[i + 4]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[i] += dpp_mov<kDppQuadXor2>(acc[i + 2]);
+      acc[0] += dpp_mov<kDppQuadXor1>(acc[1]);
+      const int tok = ts + tl;
+      if (tok < n) {
+        lg[tok] = acc[0];
+        m = fmaxf(m, acc[0]);
+      }
+    }
+  }
+  m = fmaxf(m, __shfl_xor(m, 8, 64));
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  if (tl == 0) {
+    const int h = kvh * kGroup + (j >> 1);
+    const int64_t si = ((((int64_t)b * g.L + l) * g.Hq + h) * 2 + (j & 1)) * 2;
+    a.sp.stats[si] = m;
+  }
+}
+
+// ----------------------------------------------------------------------------- select
+__global__ __launch_bounds__(256) void select_kernel(ScanArgs a) {
+  const Geo& g = a.g;
+  __shared__ uint32_t cnt[256];
+  __shared__ unsigned long long ms[256];
+  __shared__ uint32_t s_prefix, s_mask, s_above_cnt;
+  __shared__ unsigned long long s_above, s_target, s_total;
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x >> 3;
+  const int k = blockIdx.x & 7;
+  const int upr = g.L * g.Hkv;
+  const int rank = unit / upr;
+  const int rem = unit - rank * upr;
+  const int l = rem / g.Hkv;
+  const int kvh = rem - l * g.Hkv;
+  const int b = a.sp.order[rank];
+  const int h = kvh * kGroup + (k >> 1);
+  const int64_t widx = (((int64_t)b * g.L + l) * g.Hq + h) * 2 + (k & 1);
+  if (a.sp.flags[b]) {
+    if (tid == 0) a.ws_out[widx] = -1;
+    return;
+  }
+  const int n = a.sp.n_tok[b];
+  const float M = a.sp.stats[widx * 2];
+  if (n == 0) {
+    if (tid == 0) {
+      a.ws_out[widx] = 0;
+      a.sp.stats[widx * 2 + 1] = 0.f;
+      if (a.stats_out) {
+        a.stats_out[widx * 2] = M;
+        a.stats_out[widx * 2 + 1] = 0.f;
+      }
+    }
+    return;
+  }
+  const int64_t unit_base =
+      (a.sp.tok_off[b] * g.L * g.Hkv + (int64_t)(l * g.Hkv + kvh) * n) * kDists;
+  const float* x = a.sp.logits + unit_base + (int64_t)k * n;
+  if (tid == 0) {
+    s_prefix = 0;
+    s_mask = 0;
+    s_above = 0;
+    s_above_cnt = 0;
+  }
+  const bool all = a.top_p >= 1.0f;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    cnt[tid] = 0;
+    ms[tid] = 0;
+    __syncthreads();
+    const uint32_t prefix = s_prefix, mask = s_mask;
+    for (int i = tid; i < n; i += 256) {
+      const float v = x[i];
+      const uint32_t key = ord_key(v);
+      if ((key & mask) == prefix) {
+        const uint32_t bin = (key >> shift) & 255u;
+        atomicAdd(&cnt[bin], 1u);
+        atomicAdd(&ms[bin], (unsigned long long)fixed_mass(v - M));
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      if (pass == 0) {
+        unsigned long long tot = 0;
+        for (int i = 0; i < 256; ++i) tot += ms[i];
+        s_total = tot;
+        const double t = ceil((double)a.top_p * (double)tot);
+        s_target = (unsigned long long)t;
+      }
+      const unsigned long long T = s_target;
+      unsigned long long acc = s_above;
+      uint32_t c = s_above_cnt;
+      uint32_t chosen = 0;
+      for (int bin = 255; bin >= 0; --bin) {
+        if (acc + ms[bin] >= T && cnt[bin] > 0) {
+          chosen = (uint32_t)bin;
+          break;
+        }
+        acc += ms[bin];
+        c += cnt[bin];
+      }
+      s_above = acc;
+      s_above_cnt = c;
+      s_prefix = prefix | (chosen << shift);
+      s_mask = mask | (255u << shift);
+    }
+    __syncthreads();
+    if (all || s_target == 0) break;
+  }
+  if (tid == 0) {
+    int W;
+    if (all) {
+      W = n;
+    } else if (s_target == 0) {
+      W = 1;
+    } else {
+      const float vstar = ord_key_inv(s_prefix);
+      const unsigned long long q = fixed_mass(vstar - M);
+      const unsigned long long need = s_target - s_above;
+      const unsigned long long jn = q ? (need + q - 1) / q : 1ull;
+      W = (int)min((unsigned long long)n, (unsigned long long)s_above_cnt + jn);
+    }
+    a.ws_out[widx] = W;
+    const float Z = (float)((double)s_total * (1.0 / 1099511627776.0));
+    a.sp.stats[widx * 2 + 1] = Z;
+    if (a.stats_out) {
+      a.stats_out[widx * 2] = M;
+      a.stats_out[widx * 2 + 1] = Z;
+    }
+  }
+}
+
+template <bool BF16, int D>
+hipError_t launch_logits(const ScanArgs& a, int64_t units, hipStream_t st) {
+  hipLaunchKernelGGL((logit_kernel<BF16, D>), dim3((unsigned)units), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scan(const Geo& g, const ScratchPtrs& sp, int64_t max_tokens,
+                       const float* sum_s, const float* sum_l, const float* rope_cos,
+                       const float* rope_sin, int32_t rope_max_pos, const int32_t* pos,
+                       float top_p, int32_t* ws_out, float* stats_out, hipStream_t st) {
+  ScanArgs a;
+  a.g = g;
+  a.sp = sp;
+  a.max_tokens = max_tokens;
+  a.sum_s = sum_s;
+  a.sum_l = sum_l;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.rope_max_pos = rope_max_pos;
+  a.pos = pos;
+  a.scale = (float)(1.0 / sqrt((double)g.d));
+  a.top_p = top_p;
+  a.ws_out = ws_out;
+  a.stats_out = stats_out;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t units = (int64_t)g.n_req * g.L * g.Hkv;
+  if (g.dtype == GP_BF16) {
+    e = g.d == 128 ? launch_logits<true, 128>(a, units, st) : launch_logits<true, 64>(a, units, st);
+  } else {
+    e = g.d == 128 ? launch_logits<false, 128>(a, units, st) : launch_logits<false, 64>(a, units, st);
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)(units * kDists)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace gp

@@ -1,0 +1,122 @@
+"""Device state and one boundary batch through the C ABI.
+
+PyTorch is used for device memory and the stream only; every step of the boundary
+path (scan, working sets, decision, grow, keep-set, copy-on-write, compaction) runs in
+the HIP kernels of libgrowpage.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import binding as B
+
+
+@dataclasses.dataclass
+class DeviceState:
+    """Caller-owned device memory the library works on."""
+    L: int
+    Hq: int
+    Hkv: int
+    d: int
+    P: int
+    num_pages: int
+    dtype: int                  # binding.GP_F32 / GP_BF16
+    k_pool: torch.Tensor        # [L][num_pages][Hkv][P][d]
+    v_pool: torch.Tensor
+    page_table: torch.Tensor    # [max_req][max_pages] int32
+    n_alloc: torch.Tensor       # [max_req] int32
+    fill: torch.Tensor          # [max_req] int32
+    refcount: torch.Tensor      # [num_pages] int32
+    free_stack: torch.Tensor    # [num_pages] int32
+    free_top: torch.Tensor      # [1] int32
+    sum_s: torch.Tensor         # [max_req][L][Hq][d] float32
+    sum_l: torch.Tensor
+    pos: torch.Tensor           # [max_req] int32
+    rope_cos: Optional[torch.Tensor] = None   # [max_pos][d/2] float32
+    rope_sin: Optional[torch.Tensor] = None
+
+    def kv(self) -> B.KV:
+        return B.make_kv(self.k_pool, self.v_pool, self.L, self.Hq, self.Hkv, self.d, self.P,
+                         self.num_pages, self.dtype)
+
+    def pages(self) -> B.Pages:
+        return B.make_pages(self.page_table, self.n_alloc, self.fill, self.refcount,
+                            self.free_stack, self.free_top)
+
+
+@dataclasses.dataclass
+class StepOutputs:
+    ws: torch.Tensor          # [n][L][Hq][2] int32
+    stats: torch.Tensor       # [n][L][Hq][2][2] float32 (max logit, sum exp)
+    decision: torch.Tensor    # [n] uint8
+    delta: torch.Tensor       # [n] int32
+    status: torch.Tensor      # [n] int32
+    evicted: torch.Tensor     # [n][L][Hkv][P] int32
+    counters: torch.Tensor    # [GP_NUM_COUNTERS] int32
+
+
+class BoundaryEngine:
+    """Runs scan -> decide -> compact for batches of requests on one device state.
+
+    Output and scratch buffers are allocated once for a maximum batch and token count
+    and reused, so a step launches kernels only.
+    """
+
+    def __init__(self, st: DeviceState, max_batch: int, max_total_tokens: int, prm: B.Params):
+        self.st = st
+        self.prm = prm
+        self.max_total_tokens = int(max_total_tokens)
+        self.kv = st.kv()
+        self.pages = st.pages()
+        dev = st.k_pool.device
+        self.scratch_nbytes = B.scratch_bytes(self.kv, max_batch, self.max_total_tokens)
+        self.scratch = torch.empty(self.scratch_nbytes, dtype=torch.uint8, device=dev)
+        n = max_batch
+        self.out = StepOutputs(
+            ws=torch.empty((n, st.L, st.Hq, 2), dtype=torch.int32, device=dev),
+            stats=torch.empty((n, st.L, st.Hq, 2, 2), dtype=torch.float32, device=dev),
+            decision=torch.empty(n, dtype=torch.uint8, device=dev),
+            delta=torch.empty(n, dtype=torch.int32, device=dev),
+            status=torch.empty(n, dtype=torch.int32, device=dev),
+            evicted=torch.empty((n, st.L, st.Hkv, st.P), dtype=torch.int32, device=dev),
+            counters=torch.zeros(B.GP_NUM_COUNTERS, dtype=torch.int32, device=dev),
+        )
+        self.max_batch = n
+
+    def scan(self, req_ids: torch.Tensor, stream=None):
+        st, o, nb = self.st, self.out, int(req_ids.numel())
+        max_pos = 0 if st.rope_cos is None else int(st.rope_cos.shape[0])
+        B.boundary_scan(self.kv, self.pages, req_ids, nb, st.sum_s, st.sum_l, st.rope_cos,
+                        st.rope_sin, max_pos, st.pos if st.rope_cos is not None else None, self.prm,
+                        o.ws, o.stats, self.scratch, self.scratch_nbytes, self.max_total_tokens,
+                        stream)
+
+    def decide(self, req_ids: torch.Tensor, stream=None):
+        st, o, nb = self.st, self.out, int(req_ids.numel())
+        B.decide(o.ws, req_ids, nb, st.L, st.Hq, st.P, self.prm, self.pages, o.decision, o.delta,
+                 o.status, o.counters, stream)
+
+    def compact(self, req_ids: torch.Tensor, stream=None):
+        o, nb = self.out, int(req_ids.numel())
+        B.compact(self.kv, self.pages, req_ids, o.decision, nb, self.prm, o.evicted, o.status,
+                  o.counters, self.scratch, self.scratch_nbytes, self.max_total_tokens, stream)
+
+    def step(self, req_ids: torch.Tensor, stream=None) -> StepOutputs:
+        """One boundary batch: scan, decide (+grow), compact.  Asynchronous."""
+        assert req_ids.dtype == torch.int32 and req_ids.is_cuda
+        assert int(req_ids.numel()) <= self.max_batch
+        self.scan(req_ids, stream)
+        self.decide(req_ids, stream)
+        self.compact(req_ids, stream)
+        return self.out
+
+    def update_summaries(self, q: torch.Tensor, req_ids: torch.Tensor, stream=None):
+        """q: [n][L][Hq][d] float32 or bfloat16 (d contiguous)."""
+        st = self.st
+        qd = B.GP_BF16 if q.dtype == torch.bfloat16 else B.GP_F32
+        B.update_summaries(q, qd, (q.stride(0), q.stride(1), q.stride(2)), req_ids,
+                           int(req_ids.numel()), st.L, st.Hq, st.d, st.sum_s, st.sum_l, self.prm,
+                           stream)

@@ -1,0 +1,210 @@
+/*
+ * growpage.h -- C ABI of libgrowpage, the GrowPage capacity-boundary engine for
+ * AMD Instinct MI355X (CDNA4, gfx950).
+ *
+ * What the engine computes (GrowPage review on evolve.pub, section "Summary", and the
+ * paper's abstract): every request keeps two exponentially smoothed pre-RoPE query
+ * summaries per query head (short and long timescale).  When the request's last KV
+ * page fills (a capacity boundary), both summaries are scored against every retained
+ * key, the Top-p attention working-set size of each summary's softmax is taken, and
+ * the request either gets one more physical page (the recent working set is larger)
+ * or is compacted in place inside its current allocation, keeping the slots with the
+ * highest max-of-both importance.  Hyper-parameters of the paper's runs (same page,
+ * FAQ "Is GrowPage's code available?"): beta_S 0.9, beta_L 0.999, Top-p 0.99,
+ * tau 0, local retention quota 64, KV block 256.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller unless a comment says
+ *     "host".  The library keeps no state between calls and allocates no memory.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ *     Nothing is synchronised with the host; device-side outcomes (pool exhaustion,
+ *     copy-on-write shortfall) are reported per request in `status_out`.
+ *   - Argument errors are detected on the host before any launch and return
+ *     GP_ERR_INVALID (nothing is launched).  A failed launch returns GP_ERR_HIP.
+ *     Shapes the kernels do not implement return GP_ERR_UNSUPPORTED.
+ *   - `req_ids[b]` (b < n_req) names the request slot of batch entry b; all
+ *     per-request state (summaries, page-table rows, n_alloc, fill) is indexed by slot,
+ *     all outputs by batch entry.  Slots in one call must be distinct.
+ *
+ * Paged KV model (the write-page model).  Request r owns n_alloc[r] = A allocation
+ * pages page_table[r][0..A-1] plus one write page page_table[r][A] holding fill[r]
+ * tokens.  Its candidate slots are n = A*P + fill, slot i living in page i / P at
+ * offset i % P.  A boundary is fill == P.  Grow: the write page joins the allocation
+ * (A+1) and a page popped from the free stack becomes the new write page (fill 0).
+ * Compact: k = A*P slots are kept -- the last min(n_local, k) always, the others by
+ * importance (max over the KV head's query heads and both summaries of the softmax
+ * probability), an exact tie going to the more recent slot -- and are packed in slot
+ * order into slots 0..k-1 of the same pages (stable, in place); fill becomes 0.
+ * Pages are shared by all layers and heads.  A page whose refcount exceeds 1 at the
+ * start of gp_compact and whose contents would change is first copied to a fresh page
+ * (copy-on-write).  The free stack is free_stack[0 .. *free_top-1], top last.
+ */
+#ifndef GROWPAGE_H
+#define GROWPAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GP_ABI_VERSION 1
+
+typedef enum gp_status {
+  GP_OK = 0,
+  GP_ERR_INVALID = 1,      /* bad argument (NULL pointer, size, stride, alignment)    */
+  GP_ERR_HIP = 2,          /* a HIP runtime call or kernel launch failed              */
+  GP_ERR_SCRATCH = 3,      /* scratch buffer smaller than gp_scratch_bytes() asks for */
+  GP_ERR_UNSUPPORTED = 4   /* shape not implemented (see each entry point)            */
+} gp_status;
+
+typedef enum gp_dtype { GP_F32 = 0, GP_BF16 = 1 } gp_dtype;
+
+/* Per-request status bits written to status_out (device, int32). */
+#define GP_REQ_GROW_DENIED 1      /* wanted to grow; free stack empty or page-table row full: compacted */
+#define GP_REQ_DEFERRED 2         /* copy-on-write demand exceeded the free stack: left untouched      */
+#define GP_REQ_NOT_AT_BOUNDARY 4  /* fill != P: no decision applied, left untouched                    */
+#define GP_REQ_OVERFLOW 8         /* sum of candidate slots exceeded max_total_tokens: not scanned     */
+
+/* Decisions written to decision_out (device, uint8). */
+#define GP_DECISION_COMPACT 0
+#define GP_DECISION_GROW 1
+
+/* Counters written to counters_out (device, int32[GP_NUM_COUNTERS]).  gp_decide
+ * writes GROWS and GROW_DENIED; gp_compact writes the others. */
+enum {
+  GP_CNT_GROWS = 0,
+  GP_CNT_COMPACTS = 1,       /* requests compacted (not deferred)                   */
+  GP_CNT_GROW_DENIED = 2,
+  GP_CNT_DEFERRED = 3,
+  GP_CNT_COW_PAGES = 4,      /* pages copied on write                               */
+  GP_CNT_FREED_PAGES = 5,    /* pages whose refcount reached 0 and were pushed      */
+  GP_CNT_MOVED_ROWS = 6,     /* sum over compacted (layer, KV head) of rows moved   */
+  GP_CNT_COPIED_ROWS = 7,    /* rows (per layer and KV head) copied by copy-on-write */
+  GP_NUM_COUNTERS = 8
+};
+
+/* Engine parameters (host struct, passed by pointer, read during the call only). */
+typedef struct gp_params {
+  float beta_s;     /* short-timescale smoothing factor, (0, 1]                        */
+  float beta_l;     /* long-timescale smoothing factor, (0, 1]                         */
+  float top_p;      /* working-set mass threshold; >= 1 means "all n slots"            */
+  int32_t tau;      /* demand threshold: grow iff sum(W_S - W_L) > tau                 */
+  int32_t n_local;  /* most recent slots always kept by a compaction (>= 0)            */
+} gp_params;
+
+/* Paged K/V pools (host struct).  Element (layer l, page p, KV head g, slot s, i) of
+ * K lives at k + l*stride_layer + p*stride_page + g*stride_head + s*stride_tok + i
+ * (strides in elements, the d elements of a row contiguous); V likewise.  Rows must
+ * be 16-byte aligned.  Supported: Hq == 4*Hkv, d in {64, 128}, P a multiple of 8. */
+typedef struct gp_kv {
+  int32_t L, Hq, Hkv, d, P, num_pages;
+  int32_t dtype;                 /* gp_dtype of K and V */
+  void* k;                       /* device */
+  void* v;                       /* device */
+  int64_t stride_layer, stride_page, stride_head, stride_tok;
+} gp_kv;
+
+/* Page state (host struct of device pointers; all int32). */
+typedef struct gp_pages {
+  int32_t* page_table;  /* [max_req][max_pages] */
+  int32_t max_req;
+  int32_t max_pages;
+  int32_t* n_alloc;     /* [max_req] allocation pages A            */
+  int32_t* fill;        /* [max_req] tokens in the write page      */
+  int32_t* refcount;    /* [num_pages]                              */
+  int32_t* free_stack;  /* [num_pages]                              */
+  int32_t* free_top;    /* [1]                                      */
+} gp_pages;
+
+/* Version of this ABI (GP_ABI_VERSION). */
+int32_t gp_abi_version(void);
+
+/* Human-readable name of a gp_status value (static string). */
+const char* gp_status_string(int32_t status);
+
+/* Summary update, for every batch entry b, layer l, query head h and element i:
+ *   S <- beta_s*S + (1-beta_s)*q,   L <- beta_l*L + (1-beta_l)*q
+ * in float32 with each product and the sum rounded separately and (1-beta) formed in
+ * float32 (GrowPage review, "Summary": exponentially smoothed pre-RoPE summaries).
+ * q: [n_req] x [L] x [Hq] x [d] of q_dtype at element strides q_stride_req,
+ *    q_stride_layer, q_stride_head (d contiguous, 8-byte aligned rows).
+ * sum_s, sum_l: [max_req][L][Hq][d] float32, updated in place at row req_ids[b].
+ * Errors: GP_ERR_INVALID for NULL pointers, n_req < 0, d % 4 != 0. */
+gp_status gp_update_summaries(const void* q, int32_t q_dtype, int64_t q_stride_req,
+                              int64_t q_stride_layer, int64_t q_stride_head,
+                              const int32_t* req_ids, int32_t n_req, int32_t L, int32_t Hq,
+                              int32_t d, float* sum_s, float* sum_l, const gp_params* params,
+                              void* stream);
+
+/* Bytes of scratch that gp_boundary_scan and gp_compact need for a batch of n_req
+ * requests whose candidate slots sum to at most max_total_tokens. */
+size_t gp_scratch_bytes(const gp_kv* kv, int32_t n_req, int64_t max_total_tokens);
+
+/* Boundary scan (GrowPage review, "Summary": Top-p working-set sizes induced by the two
+ * summaries).  For each batch entry b (slot r = req_ids[b]), layer l and query head h,
+ * both summaries are rotated to position pos[r] (pos: [max_req] int32 by slot; positions
+ * outside the table are clamped to it) with rotate-half pairs (i, i+d/2) and the caller's
+ * table rope_cos/rope_sin [rope_max_pos][d/2] float32 (both NULL = no rotation), scored
+ * against all n = n_alloc*P + fill keys of the request (scale 1/sqrt(d)), and
+ *   ws_out[b][l][h][s] = smallest m whose m largest softmax probabilities sum >= top_p
+ * (s = 0 short, 1 long; top_p >= 1 gives n).  stats_out (optional, may be NULL):
+ * [n_req][L][Hq][2][2] float32 = (max logit, sum exp(logit - max)).  The logits and
+ * statistics are also kept in `scratch` for gp_compact, so the same scratch must be
+ * passed to gp_compact unchanged.  The page state is only read.
+ * Errors: GP_ERR_INVALID (NULL/shape), GP_ERR_SCRATCH (scratch too small),
+ * GP_ERR_UNSUPPORTED (Hq != 4*Hkv, d not 64/128, P % 8 != 0). */
+gp_status gp_boundary_scan(const gp_kv* kv, const gp_pages* pages, const int32_t* req_ids,
+                           int32_t n_req, const float* sum_s, const float* sum_l,
+                           const float* rope_cos, const float* rope_sin, int32_t rope_max_pos,
+                           const int32_t* pos, const gp_params* params, int32_t* ws_out,
+                           float* stats_out, void* scratch, size_t scratch_bytes,
+                           int64_t max_total_tokens, void* stream);
+
+/* Decision and grow (GrowPage review, "Summary": a larger recent working set triggers
+ * one extra physical page; FAQ: tau).  delta_out[b] = sum over l, h of
+ * (ws[b][l][h][0] - ws[b][l][h][1]); decision GROW iff delta > tau.  Grows pop the free
+ * stack in batch order; with the stack empty (or page_table row full) the request is
+ * compacted instead and flagged GP_REQ_GROW_DENIED.  Requests with fill != P are
+ * flagged GP_REQ_NOT_AT_BOUNDARY and left alone.  Updates page_table, n_alloc, fill,
+ * refcount (1 for popped pages) and free_top.  ws: [n_req][L][Hq][2] as written by
+ * gp_boundary_scan; P: page size (tokens).  decision_out [n_req] uint8,
+ * delta_out [n_req] int32, status_out [n_req] int32 (overwritten), counters_out
+ * (optional) int32[GP_NUM_COUNTERS]. */
+gp_status gp_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_req, int32_t L,
+                    int32_t Hq, int32_t P, const gp_params* params, const gp_pages* pages,
+                    uint8_t* decision_out, int32_t* delta_out, int32_t* status_out,
+                    int32_t* counters_out, void* stream);
+
+/* Compaction (GrowPage review, "Summary": compact within the current allocation by the
+ * maximum of both temporal importance scores; abstract: prefix caching preserved).
+ * For every batch entry with decision COMPACT and fill == P: selects the n - k evicted
+ * slots of each (layer, KV head), copies-on-write the pages that would change and are
+ * shared (snapshot refcount > 1; fresh pages popped after gp_decide's grows, in batch
+ * order and ascending page index), moves K and V rows in place, sets fill to 0,
+ * decrements the refcounts of the replaced pages and pushes the pages that reach 0 in
+ * ascending id order.  A request whose copy-on-write demand exceeds the free stack is
+ * left untouched and flagged GP_REQ_DEFERRED (status_out is OR-ed, keep gp_decide's
+ * bits).  evicted_out (optional): [n_req][L][Hkv][P] int32, ascending evicted slots,
+ * -1 padded, for compacting entries.  Needs the scratch of the preceding
+ * gp_boundary_scan of the same batch, and gp_decide's decision_out. */
+gp_status gp_compact(const gp_kv* kv, const gp_pages* pages, const int32_t* req_ids,
+                     const uint8_t* decision, int32_t n_req, const gp_params* params,
+                     int32_t* evicted_out, int32_t* status_out, int32_t* counters_out,
+                     void* scratch, size_t scratch_bytes, int64_t max_total_tokens,
+                     void* stream);
+
+/* Decode-loop helper: append one token per batch entry.  k_new, v_new:
+ * [n_req][L][Hkv][d] of kv->dtype (contiguous).  Writes slot fill[r] of the write page
+ * page_table[r][n_alloc[r]] and increments fill[r]; entries already at fill == P are
+ * skipped and flagged GP_REQ_OVERFLOW in status_out (optional, OR-ed). */
+gp_status gp_append_kv(const gp_kv* kv, const gp_pages* pages, const void* k_new,
+                       const void* v_new, const int32_t* req_ids, int32_t n_req,
+                       int32_t* status_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GROWPAGE_H */

@@ -145,6 +145,8 @@ def working_set(a: np.ndarray, p: float, band: float = NEAR_TIE):
     n = int(a.size)
     if n == 0:
         return 0, 0, 0
+    if p >= 1.0:
+        return n, n, n        # R1 fixes this case exactly; no rounding decides it
     c = np.cumsum(np.sort(np.asarray(a, np.float64))[::-1])
 
     def first(t):

@@ -1,0 +1,160 @@
+"""Element-by-element comparison of one GPU boundary batch with the CPU oracle.
+
+Exact (integers, indices, bytes): working sets, delta, decisions, status bits, evicted
+slots, page table, n_alloc, fill, refcounts, free stack and every allocation page.
+Near-ties (cumulative mass within 1e-5 of p, or the kept/evicted importance boundary
+within relative 1e-5) may resolve either way: there the GPU answer must lie in the
+oracle's range of answers, and the dependent page contents are checked as the stable
+compaction the GPU's (validated) keep-set implies.
+Floating point: max logit within 1e-3 (abs, relative above 1), sum exp within rel 1e-3.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+import oracle as O
+from synth import device as SD
+
+LOGIT_TOL = 1e-3
+Z_RTOL = 1e-3
+
+
+@dataclasses.dataclass
+class Report:
+    ws_total: int = 0
+    ws_near: int = 0
+    ev_units: int = 0
+    ev_near: int = 0
+    ev_near_differs: int = 0
+    decisions_ambiguous: int = 0
+
+
+def snapshot(st):
+    """Host copies of the page state (before a step)."""
+    return dict(page_table=st.page_table.cpu().numpy().copy(), n_alloc=st.n_alloc.cpu().numpy().copy(),
+                fill=st.fill.cpu().numpy().copy(), refcount=st.refcount.cpu().numpy().copy(),
+                free_stack=st.free_stack.cpu().numpy().copy(), free_top=int(st.free_top.item()))
+
+
+def compare_step(wl, slots, st, out, res: O.StepResult, n_local: int, check_pages=True) -> Report:
+    rep = Report()
+    Bn = wl.B
+    ws = out.ws[:Bn].cpu().numpy()
+    stats = out.stats[:Bn].cpu().numpy()
+    delta = out.delta[:Bn].cpu().numpy()
+    dec = out.decision[:Bn].cpu().numpy()
+    status = out.status[:Bn].cpu().numpy()
+    ev_gpu = out.evicted[:Bn].cpu().numpy()
+
+    # ---- working sets
+    near = res.W_lo != res.W_hi
+    rep.ws_total = int(res.W.size)
+    rep.ws_near = int(near.sum())
+    exact = ~near
+    bad = exact & (ws != res.W)
+    assert not bad.any(), f"W mismatch at {np.argwhere(bad)[:5].tolist()}: gpu {ws[bad][:5]} ref {res.W[bad][:5]}"
+    out_rng = near & ((ws < res.W_lo) | (ws > res.W_hi))
+    assert not out_rng.any(), f"W outside near-tie range at {np.argwhere(out_rng)[:5].tolist()}"
+
+    # ---- softmax statistics
+    M, Z = stats[..., 0], stats[..., 1]
+    errM = np.abs(M - res.M) / np.maximum(1.0, np.abs(res.M))
+    assert errM.max() <= LOGIT_TOL, f"max logit error {errM.max()}"
+    errZ = np.abs(Z - res.Z) / res.Z
+    assert errZ.max() <= Z_RTOL, f"sum-exp error {errZ.max()}"
+
+    # ---- decisions
+    for b in range(Bn):
+        if res.ambiguous[b]:
+            rep.decisions_ambiguous += 1
+            assert res.delta_lo[b] <= delta[b] <= res.delta_hi[b]
+        elif not near[b].any():
+            assert delta[b] == res.delta[b], (b, delta[b], res.delta[b])
+        else:
+            assert res.delta_lo[b] <= delta[b] <= res.delta_hi[b], (b, delta[b], res.delta_lo[b], res.delta_hi[b])
+    assert rep.decisions_ambiguous == 0, "seed gives an ambiguous decision; pick another"
+    assert np.array_equal(dec, res.decision), (dec, res.decision)
+    assert np.array_equal(status, res.status), (status, res.status)
+
+    # ---- keep-sets
+    gpu_kept = {}
+    for b in range(Bn):
+        if b not in res.evicted:
+            continue
+        E = res.evicted[b].shape[-1]
+        for l in range(wl.L):
+            for g in range(wl.Hkv):
+                rep.ev_units += 1
+                e_gpu = ev_gpu[b, l, g]
+                assert np.all(e_gpu[E:] == -1)
+                e_gpu = e_gpu[:E]
+                if res.evict_near_tie[b][l, g]:
+                    rep.ev_near += 1
+                    k = wl.n(b) - E
+                    assert O.keep_set_valid(e_gpu, res.imp[b][l, g], k, n_local), (b, l, g)
+                    if not np.array_equal(e_gpu, res.evicted[b][l, g]):
+                        rep.ev_near_differs += 1
+                else:
+                    assert np.array_equal(e_gpu, res.evicted[b][l, g]), (b, l, g, e_gpu, res.evicted[b][l, g])
+                gpu_kept[(b, l, g)] = np.setdiff1d(np.arange(wl.n(b)), e_gpu)
+
+    if not check_pages:
+        return rep
+    # ---- page state
+    table = st.page_table.cpu().numpy()
+    for b in range(Bn):
+        r = slots[b]
+        A = int(res.n_alloc[b])
+        assert np.array_equal(table[r, : A + 1], res.page_table[b, : A + 1]), (b, table[r, : A + 1], res.page_table[b, : A + 1])
+        assert int(st.n_alloc[r]) == A and int(st.fill[r]) == int(res.fill[b])
+    assert np.array_equal(st.refcount.cpu().numpy(), res.refcount)
+    top = int(st.free_top.item())
+    assert top == res.free_top
+    assert np.array_equal(st.free_stack.cpu().numpy()[:top], res.free_stack[:top])
+
+    # ---- page contents
+    for b in range(Bn):
+        pages = res.page_table[b]
+        if b in res.k_new:
+            k = res.k_new[b].shape[2]
+            gk, gv = SD.read_rows(st, pages, k, wl.dtype)
+            for l in range(wl.L):
+                for g in range(wl.Hkv):
+                    kept = gpu_kept[(b, l, g)]
+                    want_k = wl.k_rows[b][l, g][kept]
+                    want_v = wl.v_rows[b][l, g][kept]
+                    if not res.evict_near_tie[b][l, g]:
+                        assert np.array_equal(want_k, res.k_new[b][l, g])
+                    assert np.array_equal(gk[l, g], want_k), ("K page contents", b, l, g)
+                    assert np.array_equal(gv[l, g], want_v), ("V page contents", b, l, g)
+        else:
+            n = wl.n(b)
+            gk, gv = SD.read_rows(st, pages, n, wl.dtype)
+            assert np.array_equal(gk, wl.k_rows[b]), ("untouched K", b)
+            assert np.array_equal(gv, wl.v_rows[b]), ("untouched V", b)
+    # pages replaced by copy-on-write keep their bytes
+    for (b, j, old, new) in res.cow:
+        if res.refcount[old] > 0:
+            gk, gv = SD.read_page(st, old, wl.dtype)
+            sl = slice(j * wl.P, (j + 1) * wl.P)
+            assert np.array_equal(gk, wl.k_rows[b][:, :, sl]), ("shared page mutated", b, j, old)
+            assert np.array_equal(gv, wl.v_rows[b][:, :, sl])
+    return rep
+
+
+def run_step_gpu(wl, sum_s=None, sum_l=None, slots=None, max_req=None, params=None, tokens_budget=None):
+    """Upload ``wl``, run one boundary batch through the C ABI, synchronise."""
+    from demand_paged_kv_amd import binding as Bd
+    from demand_paged_kv_amd.engine import BoundaryEngine
+    slots = np.arange(wl.B) if slots is None else np.asarray(slots)
+    st = SD.upload(wl, "cuda", max_req=max_req, slots=slots, sum_s=sum_s, sum_l=sum_l)
+    prm = Bd.params_from(params or wl.params)
+    budget = tokens_budget or wl.total_tokens()
+    eng = BoundaryEngine(st, wl.B, budget, prm)
+    req = torch.as_tensor(slots.astype(np.int32), device="cuda")
+    out = eng.step(req)
+    torch.cuda.synchronize()
+    return st, out, eng

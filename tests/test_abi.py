@@ -1,0 +1,98 @@
+"""The C-ABI library loads and exports every symbol include/growpage.h declares; host-side
+argument validation answers without a GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from demand_paged_kv_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "growpage.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:gp_status|int32_t|size_t|const char\*)\s+(gp_\w+)\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libgrowpage.so is not built; run `python -m demand_paged_kv_amd.build`")
+    return B.load()
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared() == sorted(B.EXPORTED)
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {B.LIB_PATH}").read()
+    for name in _declared():
+        assert re.search(rf"\bT {name}$", out, re.M), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gp_abi_version() == 1
+    for s in range(5):
+        assert lib.gp_status_string(s).decode().startswith("GP_")
+    assert b"unknown" in lib.gp_status_string(99)
+
+
+def _kv(**over):
+    kv = B.make_kv(0x1000, 0x2000, 2, 32, 8, 128, 16, 1024, B.GP_BF16)
+    for k, v in over.items():
+        setattr(kv, k, v)
+    return kv
+
+
+def test_scratch_bytes_grows_with_tokens(lib):
+    kv = _kv()
+    a = B.scratch_bytes(kv, 4, 1000)
+    b = B.scratch_bytes(kv, 4, 2000)
+    # logits: 1000 more tokens x L x Hkv x 8 floats, plus importance and copy-on-write slots
+    assert b - a >= 1000 * 2 * 8 * 8 * 4
+    assert B.scratch_bytes(kv, -1, 10) == 0
+    assert lib.gp_scratch_bytes(None, 1, 1) == 0
+
+
+def test_invalid_arguments_rejected_on_host(lib):
+    kv = _kv()
+    pg = B.Pages(0x3000, 4, 8, 0x4000, 0x5000, 0x6000, 0x7000, 0x8000)
+    prm = B.params()
+    P = ctypes.byref
+    args = lambda k=kv, p=pg, pr=prm, n=1, scr=0x10000, nb=1 << 40: (
+        P(k), P(p), 0x9000, n, 0xa000, 0xb000, None, None, 0, None, P(pr), 0xc000, None, scr, nb, 10, None)
+    assert lib.gp_boundary_scan(*args(k=_kv(k=None))) == B.GP_ERR_INVALID
+    assert lib.gp_boundary_scan(*args(k=_kv(Hq=24))) == B.GP_ERR_UNSUPPORTED
+    assert lib.gp_boundary_scan(*args(k=_kv(d=96))) == B.GP_ERR_UNSUPPORTED
+    assert lib.gp_boundary_scan(*args(k=_kv(P=12))) == B.GP_ERR_UNSUPPORTED
+    assert lib.gp_boundary_scan(*args(k=_kv(stride_tok=64))) == B.GP_ERR_INVALID
+    assert lib.gp_boundary_scan(*args(k=_kv(k=0x1008))) == B.GP_ERR_INVALID
+    assert lib.gp_boundary_scan(*args(n=-1)) == B.GP_ERR_INVALID
+    assert lib.gp_boundary_scan(*args(n=5)) == B.GP_ERR_INVALID          # > max_req
+    assert lib.gp_boundary_scan(*args(nb=16)) == B.GP_ERR_SCRATCH
+    assert lib.gp_boundary_scan(*args(scr=0x10010)) == B.GP_ERR_INVALID  # scratch alignment
+    bad = B.params(beta_s=0.0)
+    assert lib.gp_boundary_scan(*args(pr=bad)) == B.GP_ERR_INVALID
+    assert lib.gp_boundary_scan(*args(n=0)) == B.GP_OK                   # empty batch: nothing launched
+    # rope table without positions
+    a = list(args())
+    a[6], a[7], a[8] = 0xd000, 0xe000, 100
+    assert lib.gp_boundary_scan(*a) == B.GP_ERR_INVALID
+    # decide / compact / ema / append
+    assert lib.gp_decide(None, 0x9000, 1, 2, 32, 16, P(prm), P(pg), 1, 2, 3, None, None) == B.GP_ERR_INVALID
+    assert lib.gp_decide(0x1, 0x9000, 1, 2, 32, 0, P(prm), P(pg), 1, 2, 3, None, None) == B.GP_ERR_INVALID
+    assert lib.gp_decide(0x1, 0x9000, 0, 2, 32, 16, P(prm), P(pg), 1, 2, 3, None, None) == B.GP_OK
+    nopool = B.Pages(0x3000, 4, 8, 0x4000, 0x5000, None, None, None)
+    assert lib.gp_decide(0x1, 0x9000, 1, 2, 32, 16, P(prm), P(nopool), 1, 2, 3, None, None) == B.GP_ERR_INVALID
+    assert lib.gp_compact(P(kv), P(pg), 0x9000, 0xa000, 1, P(prm), None, None, None, 0x10000, 1 << 40, 10, None) == B.GP_ERR_INVALID
+    assert lib.gp_compact(P(kv), P(pg), 0x9000, 0xa000, 1, P(prm), None, 0xb000, None, 0x10000, 8, 10, None) == B.GP_ERR_SCRATCH
+    assert lib.gp_update_summaries(0x1000, 1, 4, 4, 4, 0x2000, 1, 2, 8, 62, 0x3000, 0x4000, P(prm), None) == B.GP_ERR_INVALID
+    assert lib.gp_update_summaries(0x1000, 1, 4, 4, 6, 0x2000, 1, 2, 8, 64, 0x3000, 0x4000, P(prm), None) == B.GP_ERR_INVALID
+    assert lib.gp_update_summaries(0x1000, 1, 4, 4, 4, 0x2000, 0, 2, 8, 64, 0x3000, 0x4000, P(prm), None) == B.GP_OK
+    assert lib.gp_append_kv(P(kv), P(pg), None, 0x10, 0x9000, 1, None, None) == B.GP_ERR_INVALID

@@ -1,0 +1,171 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by element."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import workloads as SW
+from tests.parity_util import compare_step, run_step_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _ema_gpu(wl):
+    """Feed the decode queries through gp_update_summaries; return host summaries."""
+    from demand_paged_kv_amd import binding as Bd
+    T = wl.queries.shape[0]
+    tdt = torch.bfloat16 if wl.q_dtype == "bf16" else torch.float32
+    if wl.q_dtype == "bf16":
+        q = torch.from_numpy(np.ascontiguousarray(wl.queries).view(np.int16)).view(torch.bfloat16)
+    else:
+        q = torch.from_numpy(np.ascontiguousarray(wl.queries))
+    q = q.to("cuda")
+    assert q.dtype == tdt
+    S = torch.zeros((wl.B, wl.L, wl.Hq, wl.d), dtype=torch.float32, device="cuda")
+    Lg = torch.zeros_like(S)
+    req = torch.arange(wl.B, dtype=torch.int32, device="cuda")
+    prm = Bd.params_from(wl.params)
+    qd = Bd.GP_BF16 if wl.q_dtype == "bf16" else Bd.GP_F32
+    for t in range(T):
+        qt = q[t]
+        Bd.update_summaries(qt, qd, (qt.stride(0), qt.stride(1), qt.stride(2)), req, wl.B, wl.L,
+                            wl.Hq, wl.d, S, Lg, prm)
+    torch.cuda.synchronize()
+    return S.cpu().numpy(), Lg.cpu().numpy()
+
+
+@pytest.mark.parametrize("cfg", ["config1", "config2"])
+def test_ema_bit_exact(cfg):
+    wl = getattr(SW, cfg)()
+    _say(f"[ema] {cfg} T={wl.queries.shape[0]} B={wl.B}")
+    s_gpu, l_gpu = _ema_gpu(wl)
+    s_ref, l_ref = O.ema_run(wl.queries, wl.q_dtype, wl.params["beta_s"], wl.params["beta_l"])
+    assert np.array_equal(s_gpu.view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(l_gpu.view(np.uint32), l_ref.view(np.uint32))
+
+
+def test_ema_strided_slots():
+    """Strided q and scattered request slots update exactly the named rows."""
+    from demand_paged_kv_amd import binding as Bd
+    rng = np.random.default_rng(5)
+    n, L, Hq, d, max_req = 5, 3, 8, 64, 11
+    slots = np.array([7, 0, 3, 10, 5], np.int32)
+    big = rng.standard_normal((n, L + 1, Hq, d + 8)).astype(np.float32)
+    q = torch.from_numpy(big).cuda()[:, 1:, :, 4:4 + d]
+    s0 = rng.standard_normal((max_req, L, Hq, d)).astype(np.float32)
+    l0 = rng.standard_normal((max_req, L, Hq, d)).astype(np.float32)
+    S, Lg = torch.from_numpy(s0.copy()).cuda(), torch.from_numpy(l0.copy()).cuda()
+    prm = Bd.params(0.9, 0.999)
+    Bd.update_summaries(q, Bd.GP_F32, (q.stride(0), q.stride(1), q.stride(2)),
+                        torch.from_numpy(slots).cuda(), n, L, Hq, d, S, Lg, prm)
+    torch.cuda.synchronize()
+    want_s, want_l = s0.copy(), l0.copy()
+    qh = big[:, 1:, :, 4:4 + d]
+    for b, r in enumerate(slots):
+        want_s[r] = O.ema_update(s0[r], qh[b], 0.9)
+        want_l[r] = O.ema_update(l0[r], qh[b], 0.999)
+    assert np.array_equal(S.cpu().numpy(), want_s)
+    assert np.array_equal(Lg.cpu().numpy(), want_l)
+
+
+def test_config1_boundary():
+    wl = SW.config1()
+    _say("[step] config1")
+    s, l_ = O.ema_run(wl.queries, wl.q_dtype, wl.params["beta_s"], wl.params["beta_l"])
+    res = O.boundary_step(wl, s, l_, wl.params)
+    st, out, _ = run_step_gpu(wl, sum_s=s, sum_l=l_)
+    rep = compare_step(wl, np.arange(wl.B), st, out, res, wl.params["n_local"])
+    assert res.decision[0] == O.DECISION_COMPACT
+    _say("config1", rep)
+
+
+def test_config2_boundary():
+    wl = SW.config2()
+    _say(f"[step] config2 tokens={wl.total_tokens()}")
+    s, l_ = O.ema_run(wl.queries, wl.q_dtype, wl.params["beta_s"], wl.params["beta_l"])
+    res = O.boundary_step(wl, s, l_, wl.params)
+    assert 0 < res.counters["grows"] < wl.B
+    st, out, _ = run_step_gpu(wl, sum_s=s, sum_l=l_)
+    rep = compare_step(wl, np.arange(wl.B), st, out, res, wl.params["n_local"])
+    _say("config2", rep, res.counters)
+
+
+CASES = [
+    # (name, kwargs)
+    ("bf16_d128_p16", dict(B=6, L=2, Hq=32, Hkv=8, d=128, P=16, ctx=(100, 900))),
+    ("f32_d64_p16", dict(B=5, L=3, Hq=8, Hkv=2, d=64, P=16, dtype="f32", ctx=(30, 500))),
+    ("bf16_d64_p32", dict(B=4, L=2, Hq=8, Hkv=2, d=64, P=32, ctx=(64, 700))),
+    ("f32_d128_p8", dict(B=3, L=1, Hq=16, Hkv=4, d=128, P=8, dtype="f32", ctx=(9, 300))),
+    ("no_rope", dict(B=4, L=2, Hq=8, Hkv=2, d=64, P=16, rope=False)),
+    ("tiny_ctx", dict(B=6, L=1, Hq=8, Hkv=2, d=64, P=16, ctx=(1, 20), params=dict(SW.PARAMS_DEFAULT, n_local=4))),
+    ("local_exceeds_k", dict(B=3, L=1, Hq=8, Hkv=2, d=64, P=16, ctx=(10, 60), params=dict(SW.PARAMS_DEFAULT, n_local=1000))),
+    ("pool_exhausted", dict(B=8, L=2, Hq=8, Hkv=2, d=64, P=16, grow_frac=0.9, spare_pages=3)),
+    ("cow_prefix", dict(B=6, L=2, Hq=8, Hkv=2, d=64, P=16, grow_frac=0.2, prefix_groups=2, prefix_pages=3,
+                        ctx=(60, 200), spare_pages=40, params=dict(SW.PARAMS_DEFAULT, n_local=8))),
+    ("cow_shortfall", dict(B=5, L=1, Hq=8, Hkv=2, d=64, P=16, grow_frac=0.0, prefix_groups=1, prefix_pages=2,
+                           ctx=(40, 90), spare_pages=1, params=dict(SW.PARAMS_DEFAULT, n_local=4))),
+    ("not_at_boundary", dict(B=4, L=1, Hq=8, Hkv=2, d=64, P=16, fill=[16, 3, 16, 0])),
+    ("paper_p099", dict(B=4, L=2, Hq=32, Hkv=8, d=128, P=16, ctx=(200, 1500), params=dict(SW.PARAMS_PAPER))),
+    ("p_one", dict(B=3, L=1, Hq=8, Hkv=2, d=64, P=16, params=dict(SW.PARAMS_DEFAULT, top_p=1.0))),
+    ("p_zero", dict(B=3, L=1, Hq=8, Hkv=2, d=64, P=16, params=dict(SW.PARAMS_DEFAULT, top_p=0.0))),
+    ("table_full", dict(B=4, L=1, Hq=8, Hkv=2, d=64, P=16, grow_frac=1.0, ctx=(60, 70), max_pages=6)),
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+def test_direct_cases(name, kw):
+    wl = SW.direct_case(seed=zlib.crc32(name.encode()) % 10000, name=name, **kw)
+    _say(f"[case] {name} B={wl.B} tokens={wl.total_tokens()}")
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, wl.params)
+    # scattered request slots inside a larger table
+    slots = np.arange(wl.B) * 3 + 1
+    st, out, _ = run_step_gpu(wl, slots=slots, max_req=int(slots.max()) + 2)
+    rep = compare_step(wl, slots, st, out, res, wl.params["n_local"])
+    _say(name, rep, res.counters)
+
+
+def test_counters_config2():
+    wl = SW.config2(seed=2001)
+    s, l_ = O.ema_run(wl.queries, wl.q_dtype, wl.params["beta_s"], wl.params["beta_l"])
+    res = O.boundary_step(wl, s, l_, wl.params)
+    st, out, _ = run_step_gpu(wl, sum_s=s, sum_l=l_)
+    c = out.counters.cpu().numpy()
+    assert c[0] == res.counters["grows"] and c[1] == res.counters["compacts"]
+    assert c[2] == res.counters["grow_denied"] and c[3] == res.counters["deferred"]
+    assert c[4] == res.counters["cow_pages"] and c[5] == res.counters["freed_pages"]
+    moved = sum(max(0, wl.n(b) - wl.P - int(res.evicted[b][l, g][0]))
+                for b in res.k_new for l in range(wl.L) for g in range(wl.Hkv))
+    assert c[6] == moved
+
+
+def test_empty_batch_is_noop():
+    from demand_paged_kv_amd import binding as Bd
+    wl = SW.direct_case(seed=3, B=2, L=1, Hq=8, Hkv=2, d=64)
+    from synth import device as SD
+    st = SD.upload(wl)
+    prm = Bd.params_from(wl.params)
+    kv, pg = st.kv(), st.pages()
+    req = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Bd.boundary_scan(kv, pg, req, 0, st.sum_s, st.sum_l, None, None, 0, None, prm, req, None, req, 0, 0)
+    Bd.decide(req, req, 0, 1, 8, 16, prm, pg, req, req, req)
+    Bd.compact(kv, pg, req, req, 0, prm, None, req, None, req, 0, 0)
+    torch.cuda.synchronize()
+
+
+def test_deterministic_repeat():
+    """Two runs on the same inputs give identical bytes (integer mass sums, fixed pop order)."""
+    wl = SW.direct_case(seed=77, B=6, L=2, Hq=32, Hkv=8, d=128, P=16, ctx=(200, 2000), prefix_groups=2,
+                        prefix_pages=2, spare_pages=20, params=dict(SW.PARAMS_DEFAULT, n_local=16))
+    outs = []
+    for _ in range(2):
+        st, out, _ = run_step_gpu(wl)
+        outs.append((out.ws.cpu().numpy(), out.stats.cpu().numpy(), out.evicted.cpu().numpy(),
+                     st.k_pool.view(torch.int16).cpu().numpy(), st.page_table.cpu().numpy()))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
