@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Boundary-engine benchmark on one MI355X.
+
+Workload: the 32-layer boundary sweep on the 8B GQA shape -- 64 requests with contexts
+log-uniform in [512, 16384] tokens, 32 query / 8 KV heads, head_dim 128, bf16 K/V, page
+size 16, 30% of the requests planted as broadening demand, page ids shuffled over a
+24,576-page pool, every request at its capacity boundary.  A step is one boundary batch
+through the C ABI: gp_boundary_scan (logits of both summaries against every retained key,
+softmax statistics, Top-p working sets) -> gp_decide (delta, grow pops) ->
+gp_compact_prepare (keep-sets, copy-on-write) -> gp_compact_move (in-place K/V moves,
+free stack).  Inputs are resident in HBM before timing; between steps the mutated state is
+restored from a device copy outside the timed region, so every step sees the same batch.
+
+Prints one JSON line.  `value` is request-level boundary scans per second (each scan
+covers all 32 layers); layer-tokens scanned per second and algorithmic HBM GB/s are
+reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "KV-boundary scans/sec (tokens scanned/s) + achieved HBM GB/s vs peak, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_boundary_sweep.json")
+KERNEL_SOURCES = ["api.hip", "ema.hip", "scan.hip", "decide.hip", "compact.hip", "device_util.h",
+                  "gp_internal.h"]
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "demand_paged_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=3000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=2.0e6,
+                    help="layer-tokens of oracle work in the CPU baseline sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain 4 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def copy_probe():
+    import torch
+    n = 4 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy probe: 3 copies of {n} bytes")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the boundary engine has no multi-GPU path "
+              "(each GPU would own its own pool; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+    import numpy as np
+    import torch
+
+    from demand_paged_kv_amd import binding as Bd
+    from demand_paged_kv_amd.engine import BoundaryEngine
+    from synth import gpu_workloads as GW
+
+    Bd.load()  # the HIP library must be there; no fallback
+    t0 = time.time()
+    gw = GW.boundary_sweep(seed=args.seed)
+    st = gw.st
+    torch.cuda.synchronize()
+    log(f"workload generated in {time.time() - t0:.1f}s: {gw.B} requests, {gw.total_tokens()} tokens, "
+        f"{st.L} layers, pool {st.num_pages} pages")
+    prm = Bd.params_from(gw.params)
+    eng = BoundaryEngine(st, gw.B, gw.total_tokens(), prm)
+    req = torch.arange(gw.B, dtype=torch.int32, device="cuda")
+    backup = GW.StateBackup(st)
+    torch.cuda.synchronize()
+
+    names = ("scan", "decide", "compact_prepare", "compact_move")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    times = {k: [] for k in names}
+    totals = []
+    first = None
+    for i in range(args.warmup + args.steps):
+        backup.restore()
+        torch.cuda.synchronize()
+        ev[0].record()
+        eng.scan(req)
+        ev[1].record()
+        eng.decide(req)
+        ev[2].record()
+        eng.compact_prepare(req)
+        ev[3].record()
+        eng.compact_move(req)
+        ev[4].record()
+        torch.cuda.synchronize()
+        snap = (eng.out.decision[: gw.B].cpu().numpy().copy(), eng.out.counters.cpu().numpy().copy())
+        if first is None:
+            first = snap
+        else:
+            assert np.array_equal(first[0], snap[0]) and np.array_equal(first[1], snap[1]), "non-deterministic step"
+        if i >= args.warmup:
+            for k, name in enumerate(names):
+                times[name].append(ev[k].elapsed_time(ev[k + 1]))
+            totals.append(ev[0].elapsed_time(ev[4]))
+        log(f"step {i} ({'warmup' if i < args.warmup else 'timed'}): {ev[0].elapsed_time(ev[4]):.3f} ms")
+
+    c = dict(zip(Bd.COUNTER_NAMES, [int(x) for x in first[1]]))
+    dec = first[0]
+    L, Hkv, Hq, d, P = st.L, st.Hkv, st.Hq, st.d, st.P
+    esz = 2
+    sum_n = gw.total_tokens()
+    ms = float(np.mean(totals))
+    step_s = ms / 1e3
+    scan_bytes = L * Hkv * sum_n * d * esz + 2 * gw.B * L * Hq * d * 4
+    move_bytes = c["moved_rows"] * 4 * d * esz
+    cow_bytes = c["copied_rows"] * 4 * d * esz
+    alg_bytes = scan_bytes + move_bytes + cow_bytes
+    mean_ms = {k: float(np.mean(v)) for k, v in times.items()}
+    per_kernel = {
+        "scan": dict(bytes=scan_bytes, ms=mean_ms["scan"]),
+        "compact_move": dict(bytes=move_bytes, ms=mean_ms["compact_move"]),
+    }
+    dom = max(per_kernel, key=lambda k: per_kernel[k]["ms"])
+    kname = {"scan": "gp_boundary_scan (logit_kernel + select_kernel + plan_kernel)",
+             "compact_move": "gather_kernel (gp_compact_move)"}[dom]
+    achieved = per_kernel[dom]["bytes"] / (per_kernel[dom]["ms"] / 1e3) / 1e9
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            tf = json.load(fh)
+        if tf.get("source_hash") == source_hash() and tf.get("kernel_key") == dom:
+            traffic = tf.get("bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic}
+
+    result = {
+        "metric": METRIC,
+        "value": round(gw.B / step_s, 2),
+        "unit": "scans/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "boundary_sweep: 64 requests x 32 layers, 32q/8kv heads, d128, bf16 K/V, "
+                               "page 16, contexts log-uniform 512-16384, 30% planted broadening, "
+                               "24576-page pool",
+                   "requests": gw.B, "layers": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "page_size": P, "tokens": sum_n, "pool_pages": st.num_pages, "top_p": gw.params["top_p"],
+                   "n_local": gw.params["n_local"], "seed": args.seed, "storage_dtype": "bf16"},
+        "tokens_scanned_per_s": round(L * sum_n / step_s, 1),
+        "algorithmic_GBps": round(alg_bytes / step_s / 1e9, 1),
+        "hbm_frac": round(alg_bytes / step_s / 1e9 / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes": {"scan": scan_bytes, "compact_move": move_bytes, "copy_on_write": cow_bytes},
+        "breakdown_ms": {k: round(v, 4) for k, v in mean_ms.items()},
+        "decisions": {"grow": int((dec == 1).sum()), "compact": int((dec == 0).sum())},
+        "counters": c,
+        "roofline": roofline,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(gw, backup, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(gw, backup, budget):
+    """The oracle, as it stands, on a bounded sample of the same batch (host cores)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    from synth import gpu_workloads as GW
+
+    backup.restore()
+    torch.cuda.synchronize()
+    sample, acc = [], 0
+    for b in range(gw.B):
+        sample.append(b)
+        acc += int(gw.n[b]) * gw.st.L
+        if acc >= budget:
+            break
+    wl = GW.to_host_workload(gw, sample)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.boundary_step(wl, wl.sum_s, wl.sum_l, gw.params)
+        t = time.perf_counter() - t0
+    log(f"cpu baseline: {len(sample)} requests, {acc} layer-tokens in {t:.1f}s")
+    return {"value": round(len(sample) / t, 4), "unit": "scans/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {len(sample)} requests of the same batch ({acc} layer-tokens, all 32 layers), "
+                      f"full boundary step (scan, decide, keep-sets, compaction) in float64 numpy, 1 thread",
+            "seconds": round(t, 2), "tokens_scanned_per_s": round(acc / t, 1)}
+
+
+if __name__ == "__main__":
+    main()

@@ -23,7 +23,8 @@ COUNTER_NAMES = ("grows", "compacts", "grow_denied", "deferred", "cow_pages", "f
 GP_NUM_COUNTERS = len(COUNTER_NAMES)
 
 EXPORTED = ("gp_abi_version", "gp_status_string", "gp_update_summaries", "gp_scratch_bytes",
-            "gp_boundary_scan", "gp_decide", "gp_compact", "gp_append_kv")
+            "gp_boundary_scan", "gp_decide", "gp_compact", "gp_compact_prepare", "gp_compact_move",
+            "gp_append_kv")
 
 
 class GrowPageError(RuntimeError):
@@ -80,6 +81,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gp_compact.restype = i32
     lib.gp_compact.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Pages), P, P, i32,
                                ctypes.POINTER(Params), P, P, P, P, sz, i64, P]
+    lib.gp_compact_prepare.restype = i32
+    lib.gp_compact_prepare.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Pages), P, P, i32,
+                                       ctypes.POINTER(Params), P, P, P, sz, i64, P]
+    lib.gp_compact_move.restype = i32
+    lib.gp_compact_move.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Pages), P, i32, P, P, sz,
+                                    i64, P]
     lib.gp_append_kv.restype = i32
     lib.gp_append_kv.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Pages), P, P, P, i32, P, P]
     _lib = lib
@@ -169,6 +176,23 @@ def compact(kv: KV, pages: Pages, req_ids, decision, n_req, prm: Params, evicted
                            _ptr(counters_out), _ptr(scratch), int(scratch_nbytes),
                            int(max_total_tokens), _stream(stream))
     _check(st, "gp_compact")
+
+
+def compact_prepare(kv: KV, pages: Pages, req_ids, decision, n_req, prm: Params, evicted_out,
+                    status_out, scratch, scratch_nbytes, max_total_tokens, stream=None):
+    st = load().gp_compact_prepare(ctypes.byref(kv), ctypes.byref(pages), _ptr(req_ids),
+                                   _ptr(decision), int(n_req), ctypes.byref(prm), _ptr(evicted_out),
+                                   _ptr(status_out), _ptr(scratch), int(scratch_nbytes),
+                                   int(max_total_tokens), _stream(stream))
+    _check(st, "gp_compact_prepare")
+
+
+def compact_move(kv: KV, pages: Pages, req_ids, n_req, counters_out, scratch, scratch_nbytes,
+                 max_total_tokens, stream=None):
+    st = load().gp_compact_move(ctypes.byref(kv), ctypes.byref(pages), _ptr(req_ids), int(n_req),
+                                _ptr(counters_out), _ptr(scratch), int(scratch_nbytes),
+                                int(max_total_tokens), _stream(stream))
+    _check(st, "gp_compact_move")
 
 
 def append_kv(kv: KV, pages: Pages, k_new, v_new, req_ids, n_req, status_out=None, stream=None):

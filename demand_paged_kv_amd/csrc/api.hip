@@ -147,23 +147,59 @@ gp_status gp_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_req, in
                                 delta_out, status_out, counters_out, (hipStream_t)stream));
 }
 
-gp_status gp_compact(const gp_kv* kv, const gp_pages* pages, const int32_t* req_ids,
-                     const uint8_t* decision, int32_t n_req, const gp_params* params,
-                     int32_t* evicted_out, int32_t* status_out, int32_t* counters_out,
-                     void* scratch, size_t scratch_bytes, int64_t max_total_tokens,
-                     void* stream) {
+namespace {
+gp_status compact_checks(const gp_kv* kv, const gp_pages* pages, int32_t n_req,
+                         const gp_params* params, int64_t max_total_tokens) {
   if (gp_status s = check_kv(kv)) return s;
   if (gp_status s = check_pages(pages, true)) return s;
-  if (gp_status s = check_params(params)) return s;
+  if (params)
+    if (gp_status s = check_params(params)) return s;
   if (n_req < 0 || n_req > pages->max_req || max_total_tokens < 0) return GP_ERR_INVALID;
+  return GP_OK;
+}
+}  // namespace
+
+gp_status gp_compact_prepare(const gp_kv* kv, const gp_pages* pages, const int32_t* req_ids,
+                             const uint8_t* decision, int32_t n_req, const gp_params* params,
+                             int32_t* evicted_out, int32_t* status_out, void* scratch,
+                             size_t scratch_bytes, int64_t max_total_tokens, void* stream) {
+  if (!params) return GP_ERR_INVALID;
+  if (gp_status s = compact_checks(kv, pages, n_req, params, max_total_tokens)) return s;
   if (n_req == 0) return GP_OK;
   if (!req_ids || !decision || !status_out || !scratch) return GP_ERR_INVALID;
   if (!aligned(scratch, 256)) return GP_ERR_INVALID;
   const ScratchLayout lay = scratch_layout(*kv, n_req, max_total_tokens);
   if (scratch_bytes < lay.total) return GP_ERR_SCRATCH;
   const Geo g = make_geo(kv, pages, req_ids, n_req);
-  return from_hip(launch_compact(g, *pages, scratch_ptrs(scratch, lay), decision, params->n_local,
-                                 evicted_out, status_out, counters_out, (hipStream_t)stream));
+  return from_hip(launch_compact_prepare(g, *pages, scratch_ptrs(scratch, lay), decision,
+                                         params->n_local, evicted_out, status_out,
+                                         (hipStream_t)stream));
+}
+
+gp_status gp_compact_move(const gp_kv* kv, const gp_pages* pages, const int32_t* req_ids,
+                          int32_t n_req, int32_t* counters_out, void* scratch,
+                          size_t scratch_bytes, int64_t max_total_tokens, void* stream) {
+  if (gp_status s = compact_checks(kv, pages, n_req, nullptr, max_total_tokens)) return s;
+  if (n_req == 0) return GP_OK;
+  if (!req_ids || !scratch) return GP_ERR_INVALID;
+  if (!aligned(scratch, 256)) return GP_ERR_INVALID;
+  const ScratchLayout lay = scratch_layout(*kv, n_req, max_total_tokens);
+  if (scratch_bytes < lay.total) return GP_ERR_SCRATCH;
+  const Geo g = make_geo(kv, pages, req_ids, n_req);
+  return from_hip(launch_compact_move(g, *pages, scratch_ptrs(scratch, lay), counters_out,
+                                      (hipStream_t)stream));
+}
+
+gp_status gp_compact(const gp_kv* kv, const gp_pages* pages, const int32_t* req_ids,
+                     const uint8_t* decision, int32_t n_req, const gp_params* params,
+                     int32_t* evicted_out, int32_t* status_out, int32_t* counters_out,
+                     void* scratch, size_t scratch_bytes, int64_t max_total_tokens,
+                     void* stream) {
+  if (gp_status s = gp_compact_prepare(kv, pages, req_ids, decision, n_req, params, evicted_out,
+                                       status_out, scratch, scratch_bytes, max_total_tokens, stream))
+    return s;
+  return gp_compact_move(kv, pages, req_ids, n_req, counters_out, scratch, scratch_bytes,
+                         max_total_tokens, stream);
 }
 
 gp_status gp_append_kv(const gp_kv* kv, const gp_pages* pages, const void* k_new,

@@ -25,7 +25,7 @@
 namespace gp {
 namespace {
 
-enum { RQ_E = 0, RQ_NEED = 1, RQ_BASE = 2, RQ_STATE = 3, RQ_TOP = 4, RQ_N = 8 };
+enum { RQ_E = 0, RQ_NEED = 1, RQ_BASE = 2, RQ_STATE = 3, RQ_TOP = 4, RQ_N = kReqFields };
 enum { ST_NONE = 0, ST_PENDING = 1, ST_GO = 2, ST_DEFERRED = 3 };
 
 struct CompactArgs {
@@ -485,16 +485,23 @@ __global__ __launch_bounds__(256) void append_bump_kernel(Geo g, gp_pages pg, in
 
 }  // namespace
 
-hipError_t launch_compact(const Geo& g, const gp_pages& pg, const ScratchPtrs& sp,
-                          const uint8_t* decision, int32_t n_local, int32_t* evicted_out,
-                          int32_t* status_out, int32_t* counters_out, hipStream_t st) {
-  CompactArgs a{g, pg, sp, decision, n_local, evicted_out, status_out, counters_out};
+hipError_t launch_compact_prepare(const Geo& g, const gp_pages& pg, const ScratchPtrs& sp,
+                                  const uint8_t* decision, int32_t n_local, int32_t* evicted_out,
+                                  int32_t* status_out, hipStream_t st) {
+  CompactArgs a{g, pg, sp, decision, n_local, evicted_out, status_out, nullptr};
   const unsigned units = (unsigned)((int64_t)g.n_req * g.L * g.Hkv);
   hipLaunchKernelGGL(keep_kernel, dim3(units), dim3(256), 0, st, a);
   hipLaunchKernelGGL(req_kernel, dim3((unsigned)g.n_req), dim3(256), 0, st, a);
   hipLaunchKernelGGL(cowplan_kernel, dim3(1), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(cowassign_kernel, dim3((unsigned)g.n_req), dim3(256), 0, st, a);
   hipLaunchKernelGGL(cowcopy_kernel, dim3(2048), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact_move(const Geo& g, const gp_pages& pg, const ScratchPtrs& sp,
+                               int32_t* counters_out, hipStream_t st) {
+  CompactArgs a{g, pg, sp, nullptr, 0, nullptr, nullptr, counters_out};
+  const unsigned units = (unsigned)((int64_t)g.n_req * g.L * g.Hkv);
   const int esz = g.dtype == GP_BF16 ? 2 : 4;
   const int nv = g.d * esz / 64;  // 16-byte vectors per quarter row
   if (nv == 2)

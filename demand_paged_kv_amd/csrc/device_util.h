@@ -27,9 +27,10 @@ __device__ __forceinline__ float ord_key_inv(uint32_t k) {
 
 // exp(y) for y <= 0 as a 2^-40 fixed-point integer, truncated: exact integer sums
 // make the softmax masses and their totals independent of summation order.
+constexpr float kMassScale = 1099511627776.0f;  // 2^40
 __device__ __forceinline__ uint64_t fixed_mass(float y) {
   const float e = exp2f(y * 1.4426950408889634f);
-  return (uint64_t)(e * 1099511627776.0f);
+  return (uint64_t)(e * kMassScale);
 }
 
 // Block-wide exclusive prefix sum for blockDim.x == 256; returns the exclusive prefix of

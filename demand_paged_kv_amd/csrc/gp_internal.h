@@ -9,11 +9,10 @@
 
 namespace gp {
 
-constexpr int kWave = 64;
 constexpr int kDists = 8;          // 4 query heads per KV head x 2 summaries
 constexpr int kGroup = 4;          // query heads per KV head
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kMassScale = 1099511627776.0f;  // 2^40: fixed-point softmax mass
+constexpr int kReqFields = 8;      // per-request int32 fields of the compaction plan
 
 // ----------------------------------------------------------------------------- scratch
 // One caller buffer, carved into 256-byte aligned regions.  The scan fills the
@@ -28,7 +27,7 @@ struct ScratchLayout {
   size_t imp;       // float [tokens][L][Hkv]
   size_t ev;        // int32 [n_req][L][Hkv][P]  evicted slots, ascending
   size_t e_unit;    // int32 [n_req][L][Hkv]     first evicted slot (n if none)
-  size_t req;       // int32 [n_req][4]  e_req, cow_need, cow_base, go
+  size_t req;       // int32 [n_req][kReqFields]  first changed slot, copy-on-write plan
   size_t cow;       // int32 [cow_cap][2]  (old page, new page)
   size_t misc;      // int32 [16]  ncow, ...
   size_t bitmap;    // uint32 [num_pages/32 + 1]
@@ -58,7 +57,7 @@ inline ScratchLayout scratch_layout(const gp_kv& kv, int32_t n_req, int64_t max_
   s.imp = take(tok * kv.L * kv.Hkv * sizeof(float));
   s.ev = take(units * kv.P * sizeof(int32_t));
   s.e_unit = take(units * sizeof(int32_t));
-  s.req = take(nr * 4 * sizeof(int32_t));
+  s.req = take(nr * kReqFields * sizeof(int32_t));
   s.cow_cap = (int64_t)(tok / (kv.P > 0 ? kv.P : 1) + nr);
   s.cow = take((size_t)s.cow_cap * 2 * sizeof(int32_t));
   s.misc = take(16 * sizeof(int32_t));
@@ -135,9 +134,11 @@ hipError_t launch_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_re
                          uint8_t* decision, int32_t* delta, int32_t* status, int32_t* counters,
                          hipStream_t st);
 
-hipError_t launch_compact(const Geo& g, const gp_pages& pg, const ScratchPtrs& sp,
-                          const uint8_t* decision, int32_t n_local, int32_t* evicted_out,
-                          int32_t* status_out, int32_t* counters_out, hipStream_t st);
+hipError_t launch_compact_prepare(const Geo& g, const gp_pages& pg, const ScratchPtrs& sp,
+                                  const uint8_t* decision, int32_t n_local, int32_t* evicted_out,
+                                  int32_t* status_out, hipStream_t st);
+hipError_t launch_compact_move(const Geo& g, const gp_pages& pg, const ScratchPtrs& sp,
+                               int32_t* counters_out, hipStream_t st);
 
 hipError_t launch_append(const Geo& g, const gp_pages& pg, const void* k_new, const void* v_new,
                          int32_t* status_out, hipStream_t st);

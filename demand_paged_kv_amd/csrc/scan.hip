@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256) void select_kernel(ScanArgs a) {
       W = (int)min((unsigned long long)n, (unsigned long long)s_above_cnt + jn);
     }
     a.ws_out[widx] = W;
-    const float Z = (float)((double)s_total * (1.0 / 1099511627776.0));
+    const float Z = (float)((double)s_total / (double)kMassScale);
     a.sp.stats[widx * 2 + 1] = Z;
     if (a.stats_out) {
       a.stats_out[widx * 2] = M;

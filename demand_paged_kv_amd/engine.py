@@ -104,6 +104,16 @@ class BoundaryEngine:
         B.compact(self.kv, self.pages, req_ids, o.decision, nb, self.prm, o.evicted, o.status,
                   o.counters, self.scratch, self.scratch_nbytes, self.max_total_tokens, stream)
 
+    def compact_prepare(self, req_ids: torch.Tensor, stream=None):
+        o, nb = self.out, int(req_ids.numel())
+        B.compact_prepare(self.kv, self.pages, req_ids, o.decision, nb, self.prm, o.evicted, o.status,
+                          self.scratch, self.scratch_nbytes, self.max_total_tokens, stream)
+
+    def compact_move(self, req_ids: torch.Tensor, stream=None):
+        nb = int(req_ids.numel())
+        B.compact_move(self.kv, self.pages, req_ids, nb, self.out.counters, self.scratch,
+                       self.scratch_nbytes, self.max_total_tokens, stream)
+
     def step(self, req_ids: torch.Tensor, stream=None) -> StepOutputs:
         """One boundary batch: scan, decide (+grow), compact.  Asynchronous."""
         assert req_ids.dtype == torch.int32 and req_ids.is_cuda

@@ -195,6 +195,19 @@ gp_status gp_compact(const gp_kv* kv, const gp_pages* pages, const int32_t* req_
                      void* scratch, size_t scratch_bytes, int64_t max_total_tokens,
                      void* stream);
 
+/* The two halves of gp_compact, in this order, with the same arguments; gp_compact is
+ * exactly prepare followed by move.  prepare: keep-set selection, copy-on-write planning
+ * and page copies, page-table rewrite (writes evicted_out and GP_REQ_DEFERRED).  move:
+ * the in-place K/V row moves, refcount decrements, free-stack pushes, fill reset and
+ * counters.  Exposed so that a caller can time or overlap the row moves on their own. */
+gp_status gp_compact_prepare(const gp_kv* kv, const gp_pages* pages, const int32_t* req_ids,
+                             const uint8_t* decision, int32_t n_req, const gp_params* params,
+                             int32_t* evicted_out, int32_t* status_out, void* scratch,
+                             size_t scratch_bytes, int64_t max_total_tokens, void* stream);
+gp_status gp_compact_move(const gp_kv* kv, const gp_pages* pages, const int32_t* req_ids,
+                          int32_t n_req, int32_t* counters_out, void* scratch,
+                          size_t scratch_bytes, int64_t max_total_tokens, void* stream);
+
 /* Decode-loop helper: append one token per batch entry.  k_new, v_new:
  * [n_req][L][Hkv][d] of kv->dtype (contiguous).  Writes slot fill[r] of the write page
  * page_table[r][n_alloc[r]] and increments fill[r]; entries already at fill == P are

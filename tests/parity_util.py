@@ -145,6 +145,82 @@ def compare_step(wl, slots, st, out, res: O.StepResult, n_local: int, check_page
     return rep
 
 
+def compare_requests(wl, batch_idx, st, out, res: O.StepResult, n_local: int) -> Report:
+    """Per-request checks for a sample of a larger batch: ``res`` is the oracle run on the
+    sampled requests alone (``wl`` holds them in order), ``batch_idx[i]`` is the position of
+    sampled request i in the GPU batch (request slot == batch position).  Page ids of newly
+    popped pages depend on the whole batch and are checked by ``check_pool``."""
+    rep = Report()
+    idx = np.asarray(batch_idx)
+    ws = out.ws.cpu().numpy()[idx]
+    stats = out.stats.cpu().numpy()[idx]
+    delta = out.delta.cpu().numpy()[idx]
+    dec = out.decision.cpu().numpy()[idx]
+    status = out.status.cpu().numpy()[idx]
+    ev_gpu = out.evicted.cpu().numpy()[idx]
+    near = res.W_lo != res.W_hi
+    rep.ws_total, rep.ws_near = int(res.W.size), int(near.sum())
+    assert not (~near & (ws != res.W)).any(), "W mismatch"
+    assert not (near & ((ws < res.W_lo) | (ws > res.W_hi))).any(), "W outside near-tie range"
+    errM = np.abs(stats[..., 0] - res.M) / np.maximum(1.0, np.abs(res.M))
+    errZ = np.abs(stats[..., 1] - res.Z) / res.Z
+    assert errM.max() <= LOGIT_TOL and errZ.max() <= Z_RTOL, (errM.max(), errZ.max())
+    for i in range(len(idx)):
+        assert not res.ambiguous[i], "ambiguous decision in the sample"
+        assert res.delta_lo[i] <= delta[i] <= res.delta_hi[i]
+        if not near[i].any():
+            assert delta[i] == res.delta[i]
+    assert np.array_equal(dec, res.decision) and np.array_equal(status, res.status)
+    table = st.page_table.cpu().numpy()
+    for i, b in enumerate(idx):
+        pages = table[b]
+        if i in res.evicted:
+            E = res.evicted[i].shape[-1]
+            k = wl.n(i) - E
+            gk, gv = SD.read_rows(st, pages, k, wl.dtype)
+            for l in range(wl.L):
+                for g in range(wl.Hkv):
+                    rep.ev_units += 1
+                    e = ev_gpu[i, l, g, :E]
+                    if res.evict_near_tie[i][l, g]:
+                        rep.ev_near += 1
+                        assert O.keep_set_valid(e, res.imp[i][l, g], k, n_local)
+                    else:
+                        assert np.array_equal(e, res.evicted[i][l, g]), (i, l, g)
+                    kept = np.setdiff1d(np.arange(wl.n(i)), e)
+                    assert np.array_equal(gk[l, g], wl.k_rows[i][l, g][kept]), ("K", i, l, g)
+                    assert np.array_equal(gv[l, g], wl.v_rows[i][l, g][kept]), ("V", i, l, g)
+        else:
+            gk, gv = SD.read_rows(st, pages, wl.n(i), wl.dtype)
+            assert np.array_equal(gk, wl.k_rows[i]) and np.array_equal(gv, wl.v_rows[i]), ("untouched", i)
+    return rep
+
+
+def check_pool(st, before: dict, decision: np.ndarray, slots: np.ndarray):
+    """Pool-wide invariants after a batch without sharing: grows popped the top of the
+    free stack in batch order, every page referenced once, free + referenced = pool."""
+    table = st.page_table.cpu().numpy()
+    n_alloc = st.n_alloc.cpu().numpy()
+    rc = st.refcount.cpu().numpy()
+    top0, stack0 = before["free_top"], before["free_stack"]
+    growers = [b for b in range(len(slots)) if decision[b] == 1]
+    for rank, b in enumerate(growers):
+        r = slots[b]
+        assert table[r, n_alloc[r]] == stack0[top0 - 1 - rank]
+        assert n_alloc[r] == before["n_alloc"][r] + 1
+    top = int(st.free_top.item())
+    assert top == top0 - len(growers)
+    refs = np.zeros_like(rc)
+    for r in range(table.shape[0]):
+        for j in range(int(n_alloc[r]) + 1):
+            if table[r, j] >= 0:
+                refs[table[r, j]] += 1
+    assert np.array_equal(refs, rc)
+    free = st.free_stack.cpu().numpy()[:top]
+    assert np.unique(free).size == top and np.all(rc[free] == 0)
+    assert top + np.count_nonzero(refs) == rc.size
+
+
 def run_step_gpu(wl, sum_s=None, sum_l=None, slots=None, max_req=None, params=None, tokens_budget=None):
     """Upload ``wl``, run one boundary batch through the C ABI, synchronise."""
     from demand_paged_kv_amd import binding as Bd

@@ -1,0 +1,40 @@
+"""Full-size parity on the benchmark workload (32-layer boundary sweep on the 8B GQA
+shape, generated on the GPU), in the launch configuration bench.py times: the oracle
+recomputes a sample of requests end to end (working sets, statistics, decision,
+keep-sets, compacted page bytes); the whole batch is checked by pool invariants."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from tests.parity_util import check_pool, compare_requests, snapshot
+
+pytestmark = pytest.mark.gpu
+
+
+def test_boundary_sweep_full_size_sampled():
+    from demand_paged_kv_amd import binding as Bd
+    from demand_paged_kv_amd.engine import BoundaryEngine
+    from synth import gpu_workloads as GW
+
+    gw = GW.boundary_sweep(seed=3000)
+    st = gw.st
+    print(f"[fullsize] generated {gw.B} requests, {gw.total_tokens()} tokens", flush=True)
+    order = np.argsort(-gw.n)
+    sample = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]),
+                     int(np.flatnonzero(gw.regime == 1)[0]), int(np.flatnonzero(gw.regime == 0)[0]),
+                     int(np.flatnonzero(gw.regime == 1)[-1])})
+    wl = GW.to_host_workload(gw, sample)
+    before = snapshot(st)
+    eng = BoundaryEngine(st, gw.B, gw.total_tokens(), Bd.params_from(gw.params))
+    req = torch.arange(gw.B, dtype=torch.int32, device="cuda")
+    out = eng.step(req)
+    torch.cuda.synchronize()
+    print("[fullsize] step done; oracle on sample", sample, flush=True)
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, gw.params)
+    rep = compare_requests(wl, sample, st, out, res, gw.params["n_local"])
+    dec = out.decision.cpu().numpy()
+    check_pool(st, before, dec, np.arange(gw.B))
+    # planted regimes come out as planted
+    assert np.array_equal(dec, gw.regime.astype(np.uint8)), (dec, gw.regime)
+    print("[fullsize]", rep, flush=True)

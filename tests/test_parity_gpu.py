@@ -108,6 +108,8 @@ CASES = [
     ("pool_exhausted", dict(B=8, L=2, Hq=8, Hkv=2, d=64, P=16, grow_frac=0.9, spare_pages=3)),
     ("cow_prefix", dict(B=6, L=2, Hq=8, Hkv=2, d=64, P=16, grow_frac=0.2, prefix_groups=2, prefix_pages=3,
                         ctx=(60, 200), spare_pages=40, params=dict(SW.PARAMS_DEFAULT, n_local=8))),
+    ("cow_many", dict(B=24, L=1, Hq=8, Hkv=2, d=64, P=16, grow_frac=0.25, prefix_groups=4, prefix_pages=2,
+                      ctx=(40, 160), spare_pages=30, params=dict(SW.PARAMS_DEFAULT, n_local=4))),
     ("cow_shortfall", dict(B=5, L=1, Hq=8, Hkv=2, d=64, P=16, grow_frac=0.0, prefix_groups=1, prefix_pages=2,
                            ctx=(40, 90), spare_pages=1, params=dict(SW.PARAMS_DEFAULT, n_local=4))),
     ("not_at_boundary", dict(B=4, L=1, Hq=8, Hkv=2, d=64, P=16, fill=[16, 3, 16, 0])),
