@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "KV-boundary scans/sec (tokens scanned/s) + achieved HBM GB/s vs peak, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_boundary_sweep.json")
-KERNEL_SOURCES = ["api.hip", "ema.hip", "scan.hip", "decide.hip", "compact.hip", "device_util.h",
+KERNEL_SOURCES = ["api.hip", "ema.hip", "scan.hip", "finish.hip", "decide.hip", "compact.hip", "device_util.h",
                   "gp_internal.h"]
 
 
@@ -145,7 +145,7 @@ def main():
         "compact_move": dict(bytes=move_bytes, ms=mean_ms["compact_move"]),
     }
     dom = max(per_kernel, key=lambda k: per_kernel[k]["ms"])
-    kname = {"scan": "gp_boundary_scan (logit_kernel + select_kernel + plan_kernel)",
+    kname = {"scan": "gp_boundary_scan (plan_kernel + logit_kernel + finish_kernel)",
              "compact_move": "gather_kernel (gp_compact_move)"}[dom]
     achieved = per_kernel[dom]["bytes"] / (per_kernel[dom]["ms"] / 1e3) / 1e9
     traffic = None

@@ -130,8 +130,8 @@ gp_status gp_boundary_scan(const gp_kv* kv, const gp_pages* pages, const int32_t
   if (scratch_bytes < lay.total) return GP_ERR_SCRATCH;
   const Geo g = make_geo(kv, pages, req_ids, n_req);
   return from_hip(launch_scan(g, scratch_ptrs(scratch, lay), max_total_tokens, sum_s, sum_l, rope_cos,
-                              rope_sin, rope_max_pos, pos, params->top_p, ws_out, stats_out,
-                              (hipStream_t)stream));
+                              rope_sin, rope_max_pos, pos, params->top_p, params->n_local,
+                              ws_out, stats_out, (hipStream_t)stream));
 }
 
 gp_status gp_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_req, int32_t L,
@@ -172,8 +172,7 @@ gp_status gp_compact_prepare(const gp_kv* kv, const gp_pages* pages, const int32
   if (scratch_bytes < lay.total) return GP_ERR_SCRATCH;
   const Geo g = make_geo(kv, pages, req_ids, n_req);
   return from_hip(launch_compact_prepare(g, *pages, scratch_ptrs(scratch, lay), decision,
-                                         params->n_local, evicted_out, status_out,
-                                         (hipStream_t)stream));
+                                         evicted_out, status_out, (hipStream_t)stream));
 }
 
 gp_status gp_compact_move(const gp_kv* kv, const gp_pages* pages, const int32_t* req_ids,

@@ -4,9 +4,9 @@
 // quota 64; abstract: page-level integration keeps prefix caching).
 //
 // Launch sequence for one batch (all on the caller's stream, no host round trip):
-//   keep_kernel      per (entry, layer, KV head) unit of a compacting entry: importance
-//                    = max over the 8 softmax rows, exact radix select of the n-k least
-//                    important candidates (ties: older slot first), ascending list.
+//   (the keep-sets -- the n-k least important candidate slots of each (entry, layer,
+//    KV head) unit, ties to the older slot -- come from the scan's finish kernel)
+//   publish_kernel   copy the keep-sets of compacting entries to the caller (optional).
 //   req_kernel       per entry: first changed slot e (min over units), copy-on-write
 //                    demand = shared pages (refcount > 1) at index >= e / P.
 //   cowplan_kernel   1 block: greedy in batch order -- an entry whose demand fits the
@@ -33,7 +33,7 @@ struct CompactArgs {
   gp_pages pg;
   ScratchPtrs sp;
   const uint8_t* decision;
-  int32_t n_local;
+  int32_t unused;
   int32_t* evicted_out;
   int32_t* status_out;
   int32_t* counters_out;
@@ -54,109 +54,18 @@ __device__ __forceinline__ bool is_compacting(const CompactArgs& a, int b, int r
 }
 
 // ----------------------------------------------------------------------------- keep-set
-__global__ __launch_bounds__(256) void keep_kernel(CompactArgs a) {
+// The keep-sets themselves are selected by the scan's finish kernel; here they are only
+// published to the caller for the entries that compact.
+__global__ __launch_bounds__(64) void publish_kernel(CompactArgs a) {
   const Geo& g = a.g;
-  __shared__ int tmp[4];
-  __shared__ uint32_t cnt[256];
-  __shared__ uint32_t s_prefix, s_mask, s_below;
-  __shared__ int s_eqc, s_outc;
-  __shared__ float s_M[kDists], s_iz[kDists];
-  const int tid = threadIdx.x;
-  int b, l, kvh;
-  unit_of_block(g, a.sp, blockIdx.x, b, l, kvh);
-  const int64_t u = ((int64_t)b * g.L + l) * g.Hkv + kvh;
+  const int64_t u = blockIdx.x;
+  const int upr = g.L * g.Hkv;
+  const int b = (int)(u / upr);
   const int r = g.req_ids[b];
   const int P = g.P;
-  if (!is_compacting(a, b, r)) {
-    if (a.evicted_out)
-      for (int i = tid; i < P; i += 256) a.evicted_out[u * P + i] = -1;
-    if (tid == 0) a.sp.e_unit[u] = 0x7fffffff;
-    return;
-  }
-  const int n = a.sp.n_tok[b];
-  const int k = g.n_alloc[r] * P;
-  const int E = n - k;
-  const int nl = min(max(a.n_local, 0), k);
-  const int cand = n - nl;
-  if (tid < kDists) {
-    const int h = kvh * kGroup + (tid >> 1);
-    const int64_t si = ((((int64_t)b * g.L + l) * g.Hq + h) * 2 + (tid & 1)) * 2;
-    s_M[tid] = a.sp.stats[si];
-    s_iz[tid] = 1.0f / a.sp.stats[si + 1];
-  }
-  __syncthreads();
-  const int64_t unit_base = (a.sp.tok_off[b] * g.L * g.Hkv + (int64_t)(l * g.Hkv + kvh) * n);
-  const float* x = a.sp.logits + unit_base * kDists;
-  float* imp = a.sp.imp + unit_base;
-  for (int i = tid; i < cand; i += 256) {
-    float v = 0.f;
-#pragma unroll
-    for (int q = 0; q < kDists; ++q)
-      v = fmaxf(v, exp2f((x[(int64_t)q * n + i] - s_M[q]) * kLog2e) * s_iz[q]);
-    imp[i] = v;
-  }
-  if (tid == 0) {
-    s_prefix = 0;
-    s_mask = 0;
-    s_below = 0;
-    s_eqc = 0;
-    s_outc = 0;
-  }
-  __syncthreads();
-  if (E > 0) {
-    // E-th smallest importance key (importance >= 0, so its float bits are ordered).
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      cnt[tid] = 0;
-      __syncthreads();
-      const uint32_t prefix = s_prefix, mask = s_mask;
-      for (int i = tid; i < cand; i += 256) {
-        const uint32_t key = __float_as_uint(imp[i]);
-        if ((key & mask) == prefix) atomicAdd(&cnt[(key >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t acc = s_below, chosen = 255;
-        for (int bin = 0; bin < 256; ++bin) {
-          if (acc + cnt[bin] >= (uint32_t)E) {
-            chosen = (uint32_t)bin;
-            break;
-          }
-          acc += cnt[bin];
-        }
-        s_below = acc;
-        s_prefix = prefix | (chosen << shift);
-        s_mask = mask | (255u << shift);
-      }
-      __syncthreads();
-    }
-    const uint32_t kstar = s_prefix;
-    const int need = E - (int)s_below;
-    for (int base = 0; base < cand; base += 256) {
-      const int i = base + tid;
-      const uint32_t key = i < cand ? __float_as_uint(imp[i]) : 0xffffffffu;
-      const int lt = (i < cand && key < kstar) ? 1 : 0;
-      const int eq = (i < cand && key == kstar) ? 1 : 0;
-      int eqtot = 0, ftot = 0;
-      const int eqr = s_eqc + block_exscan_256(eq, tmp, &eqtot);
-      const int flag = (lt || (eq && eqr < need)) ? 1 : 0;
-      const int pos = s_outc + block_exscan_256(flag, tmp, &ftot);
-      if (flag && pos < E) {
-        a.sp.ev[u * P + pos] = i;
-        if (a.evicted_out) a.evicted_out[u * P + pos] = i;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        s_eqc += eqtot;
-        s_outc += ftot;
-      }
-      __syncthreads();
-    }
-  }
-  if (a.evicted_out)
-    for (int i = E + tid; i < P; i += 256) a.evicted_out[u * P + i] = -1;
-  __syncthreads();
-  if (tid == 0) a.sp.e_unit[u] = E > 0 ? a.sp.ev[u * P] : n;
+  const bool comp = is_compacting(a, b, r);
+  const int E = comp ? a.sp.n_tok[b] - g.n_alloc[r] * P : 0;
+  for (int i = threadIdx.x; i < P; i += 64) a.evicted_out[u * P + i] = i < E ? a.sp.ev[u * P + i] : -1;
 }
 
 // ----------------------------------------------------------------------------- per entry
@@ -486,11 +395,11 @@ __global__ __launch_bounds__(256) void append_bump_kernel(Geo g, gp_pages pg, in
 }  // namespace
 
 hipError_t launch_compact_prepare(const Geo& g, const gp_pages& pg, const ScratchPtrs& sp,
-                                  const uint8_t* decision, int32_t n_local, int32_t* evicted_out,
+                                  const uint8_t* decision, int32_t* evicted_out,
                                   int32_t* status_out, hipStream_t st) {
-  CompactArgs a{g, pg, sp, decision, n_local, evicted_out, status_out, nullptr};
+  CompactArgs a{g, pg, sp, decision, 0, evicted_out, status_out, nullptr};
   const unsigned units = (unsigned)((int64_t)g.n_req * g.L * g.Hkv);
-  hipLaunchKernelGGL(keep_kernel, dim3(units), dim3(256), 0, st, a);
+  if (evicted_out) hipLaunchKernelGGL(publish_kernel, dim3(units), dim3(64), 0, st, a);
   hipLaunchKernelGGL(req_kernel, dim3((unsigned)g.n_req), dim3(256), 0, st, a);
   hipLaunchKernelGGL(cowplan_kernel, dim3(1), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(cowassign_kernel, dim3((unsigned)g.n_req), dim3(256), 0, st, a);

@@ -23,10 +23,9 @@ struct ScratchLayout {
   size_t order;     // int32 [n_req]  entries by n descending (ties by index)
   size_t flags;     // int32 [n_req]  GP_REQ_OVERFLOW when over budget
   size_t stats;     // float [n_req][L][Hq][2][2]  max logit, sum exp
-  size_t logits;    // float [tokens][L][Hkv][8] (per unit: [8][n])
-  size_t imp;       // float [tokens][L][Hkv]
-  size_t ev;        // int32 [n_req][L][Hkv][P]  evicted slots, ascending
-  size_t e_unit;    // int32 [n_req][L][Hkv]     first evicted slot (n if none)
+  size_t logits;    // float [tokens][L][Hkv][8] (per unit: [n][8], token-major)
+  size_t ev;        // int32 [n_req][L][Hkv][P]  slots a compaction evicts, ascending
+  size_t e_unit;    // int32 [n_req][L][Hkv]     first of them (n if none)
   size_t req;       // int32 [n_req][kReqFields]  first changed slot, copy-on-write plan
   size_t cow;       // int32 [cow_cap][2]  (old page, new page)
   size_t misc;      // int32 [16]  ncow, ...
@@ -54,7 +53,6 @@ inline ScratchLayout scratch_layout(const gp_kv& kv, int32_t n_req, int64_t max_
   s.flags = take(nr * sizeof(int32_t));
   s.stats = take(nr * kv.L * kv.Hq * 4 * sizeof(float));
   s.logits = take(tok * kv.L * kv.Hkv * kDists * sizeof(float));
-  s.imp = take(tok * kv.L * kv.Hkv * sizeof(float));
   s.ev = take(units * kv.P * sizeof(int32_t));
   s.e_unit = take(units * sizeof(int32_t));
   s.req = take(nr * kReqFields * sizeof(int32_t));
@@ -74,7 +72,6 @@ struct ScratchPtrs {
   int32_t* flags;
   float* stats;
   float* logits;
-  float* imp;
   int32_t* ev;
   int32_t* e_unit;
   int32_t* req;
@@ -93,7 +90,6 @@ inline ScratchPtrs scratch_ptrs(void* base, const ScratchLayout& s) {
   p.flags = (int32_t*)(b + s.flags);
   p.stats = (float*)(b + s.stats);
   p.logits = (float*)(b + s.logits);
-  p.imp = (float*)(b + s.imp);
   p.ev = (int32_t*)(b + s.ev);
   p.e_unit = (int32_t*)(b + s.e_unit);
   p.req = (int32_t*)(b + s.req);
@@ -127,7 +123,18 @@ hipError_t launch_ema(const void* q, int32_t q_dtype, int64_t sr, int64_t sl, in
 hipError_t launch_scan(const Geo& g, const ScratchPtrs& sp, int64_t max_tokens,
                        const float* sum_s, const float* sum_l, const float* rope_cos,
                        const float* rope_sin, int32_t rope_max_pos, const int32_t* pos,
-                       float top_p, int32_t* ws_out, float* stats_out, hipStream_t st);
+                       float top_p, int32_t n_local, int32_t* ws_out, float* stats_out,
+                       hipStream_t st);
+
+struct FinishArgs {
+  Geo g;
+  ScratchPtrs sp;
+  float top_p;
+  int32_t n_local;
+  int32_t* ws_out;
+  float* stats_out;
+};
+hipError_t launch_finish(const FinishArgs& a, hipStream_t st);
 
 hipError_t launch_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_req, int32_t L,
                          int32_t Hq, int32_t tau, const gp_pages& pg, int32_t P,
@@ -135,7 +142,7 @@ hipError_t launch_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_re
                          hipStream_t st);
 
 hipError_t launch_compact_prepare(const Geo& g, const gp_pages& pg, const ScratchPtrs& sp,
-                                  const uint8_t* decision, int32_t n_local, int32_t* evicted_out,
+                                  const uint8_t* decision, int32_t* evicted_out,
                                   int32_t* status_out, hipStream_t st);
 hipError_t launch_compact_move(const Geo& g, const gp_pages& pg, const ScratchPtrs& sp,
                                int32_t* counters_out, hipStream_t st);

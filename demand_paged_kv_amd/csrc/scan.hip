@@ -3,7 +3,7 @@
 // (GrowPage review on evolve.pub, "Summary": compare the Top-p attention working-set
 // sizes induced by the short- and long-timescale summaries, kept pre-RoPE.)
 //
-// Three launches:
+// Three launches (the third, finish_kernel, lives in finish.hip):
 //   plan_kernel    1 block: candidate slots n of every batch entry, token offsets into
 //                  the scratch, and a longest-first order of the entries.
 //   logit_kernel   one wave per (entry, layer, KV head) "unit", launched longest-first.
@@ -12,11 +12,10 @@
 //                  keeps the matching slices of all 8 rotated summaries (4 query heads x
 //                  2 timescales) in registers, and a 3-step DPP transpose-reduce leaves
 //                  lane j with the logit of summary j for its token.  Logits go to the
-//                  scratch ([unit][8][n] float32), the running max to the statistics.
-//   select_kernel  one 256-thread block per (unit, summary): exact radix select on the
-//                  ordered float key of the logits (4 passes of 8 bits), weighted by the
-//                  softmax mass exp(l - M) in 2^-40 fixed point (order-independent sums),
-//                  gives the smallest m whose m largest probabilities reach top_p.
+//                  scratch ([unit][n][8] float32: one wave step writes 256 contiguous
+//                  bytes), the running max to the statistics.
+//   finish_kernel  one block per unit: exact Top-p working sets of the 8 logit rows and
+//                  the unit's keep-set, from two reads of the logits.
 #include "device_util.h"
 #include "gp_internal.h"
 
@@ -34,9 +33,7 @@ struct ScanArgs {
   int32_t rope_max_pos;
   const int32_t* pos;
   float scale;
-  float top_p;
   int32_t* ws_out;
-  float* stats_out;
 };
 
 // ----------------------------------------------------------------------------- plan
@@ -226,7 +223,7 @@ __global__ __launch_bounds__(64) void logit_kernel(ScanArgs a) {
 
   const int64_t unit_base =
       (a.sp.tok_off[b] * g.L * g.Hkv + (int64_t)(l * g.Hkv + kvh) * n) * kDists;
-  float* lg = a.sp.logits + unit_base + (int64_t)j * n;
+  float* lg = a.sp.logits + unit_base + j;  // token-major: [n][8]
   const char* kb = reinterpret_cast<const char*>(g.k) + ((int64_t)l * g.s_layer + (int64_t)kvh * g.s_head) * E;
   const int32_t* pt = g.page_table + (int64_t)r * g.max_pages;
   float m = -INFINITY;
@@ -264,7 +261,7 @@ __global__ __launch_bounds__(64) void logit_kernel(ScanArgs a) {
       acc[0] += dpp_mov<kDppQuadXor1>(acc[1]);
       const int tok = ts + tl;
       if (tok < n) {
-        lg[tok] = acc[0];
+        lg[(int64_t)tok * kDists] = acc[0];
         m = fmaxf(m, acc[0]);
       }
     }
@@ -279,118 +276,6 @@ __global__ __launch_bounds__(64) void logit_kernel(ScanArgs a) {
   }
 }
 
-// ----------------------------------------------------------------------------- select
-__global__ __launch_bounds__(256) void select_kernel(ScanArgs a) {
-  const Geo& g = a.g;
-  __shared__ uint32_t cnt[256];
-  __shared__ unsigned long long ms[256];
-  __shared__ uint32_t s_prefix, s_mask, s_above_cnt;
-  __shared__ unsigned long long s_above, s_target, s_total;
-  const int tid = threadIdx.x;
-  const int unit = blockIdx.x >> 3;
-  const int k = blockIdx.x & 7;
-  const int upr = g.L * g.Hkv;
-  const int rank = unit / upr;
-  const int rem = unit - rank * upr;
-  const int l = rem / g.Hkv;
-  const int kvh = rem - l * g.Hkv;
-  const int b = a.sp.order[rank];
-  const int h = kvh * kGroup + (k >> 1);
-  const int64_t widx = (((int64_t)b * g.L + l) * g.Hq + h) * 2 + (k & 1);
-  if (a.sp.flags[b]) {
-    if (tid == 0) a.ws_out[widx] = -1;
-    return;
-  }
-  const int n = a.sp.n_tok[b];
-  const float M = a.sp.stats[widx * 2];
-  if (n == 0) {
-    if (tid == 0) {
-      a.ws_out[widx] = 0;
-      a.sp.stats[widx * 2 + 1] = 0.f;
-      if (a.stats_out) {
-        a.stats_out[widx * 2] = M;
-        a.stats_out[widx * 2 + 1] = 0.f;
-      }
-    }
-    return;
-  }
-  const int64_t unit_base =
-      (a.sp.tok_off[b] * g.L * g.Hkv + (int64_t)(l * g.Hkv + kvh) * n) * kDists;
-  const float* x = a.sp.logits + unit_base + (int64_t)k * n;
-  if (tid == 0) {
-    s_prefix = 0;
-    s_mask = 0;
-    s_above = 0;
-    s_above_cnt = 0;
-  }
-  const bool all = a.top_p >= 1.0f;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    cnt[tid] = 0;
-    ms[tid] = 0;
-    __syncthreads();
-    const uint32_t prefix = s_prefix, mask = s_mask;
-    for (int i = tid; i < n; i += 256) {
-      const float v = x[i];
-      const uint32_t key = ord_key(v);
-      if ((key & mask) == prefix) {
-        const uint32_t bin = (key >> shift) & 255u;
-        atomicAdd(&cnt[bin], 1u);
-        atomicAdd(&ms[bin], (unsigned long long)fixed_mass(v - M));
-      }
-    }
-    __syncthreads();
-    if (tid == 0) {
-      if (pass == 0) {
-        unsigned long long tot = 0;
-        for (int i = 0; i < 256; ++i) tot += ms[i];
-        s_total = tot;
-        const double t = ceil((double)a.top_p * (double)tot);
-        s_target = (unsigned long long)t;
-      }
-      const unsigned long long T = s_target;
-      unsigned long long acc = s_above;
-      uint32_t c = s_above_cnt;
-      uint32_t chosen = 0;
-      for (int bin = 255; bin >= 0; --bin) {
-        if (acc + ms[bin] >= T && cnt[bin] > 0) {
-          chosen = (uint32_t)bin;
-          break;
-        }
-        acc += ms[bin];
-        c += cnt[bin];
-      }
-      s_above = acc;
-      s_above_cnt = c;
-      s_prefix = prefix | (chosen << shift);
-      s_mask = mask | (255u << shift);
-    }
-    __syncthreads();
-    if (all || s_target == 0) break;
-  }
-  if (tid == 0) {
-    int W;
-    if (all) {
-      W = n;
-    } else if (s_target == 0) {
-      W = 1;
-    } else {
-      const float vstar = ord_key_inv(s_prefix);
-      const unsigned long long q = fixed_mass(vstar - M);
-      const unsigned long long need = s_target - s_above;
-      const unsigned long long jn = q ? (need + q - 1) / q : 1ull;
-      W = (int)min((unsigned long long)n, (unsigned long long)s_above_cnt + jn);
-    }
-    a.ws_out[widx] = W;
-    const float Z = (float)((double)s_total / (double)kMassScale);
-    a.sp.stats[widx * 2 + 1] = Z;
-    if (a.stats_out) {
-      a.stats_out[widx * 2] = M;
-      a.stats_out[widx * 2 + 1] = Z;
-    }
-  }
-}
-
 template <bool BF16, int D>
 hipError_t launch_logits(const ScanArgs& a, int64_t units, hipStream_t st) {
   hipLaunchKernelGGL((logit_kernel<BF16, D>), dim3((unsigned)units), dim3(64), 0, st, a);
@@ -402,7 +287,8 @@ hipError_t launch_logits(const ScanArgs& a, int64_t units, hipStream_t st) {
 hipError_t launch_scan(const Geo& g, const ScratchPtrs& sp, int64_t max_tokens,
                        const float* sum_s, const float* sum_l, const float* rope_cos,
                        const float* rope_sin, int32_t rope_max_pos, const int32_t* pos,
-                       float top_p, int32_t* ws_out, float* stats_out, hipStream_t st) {
+                       float top_p, int32_t n_local, int32_t* ws_out, float* stats_out,
+                       hipStream_t st) {
   ScanArgs a;
   a.g = g;
   a.sp = sp;
@@ -414,9 +300,7 @@ hipError_t launch_scan(const Geo& g, const ScratchPtrs& sp, int64_t max_tokens,
   a.rope_max_pos = rope_max_pos;
   a.pos = pos;
   a.scale = (float)(1.0 / sqrt((double)g.d));
-  a.top_p = top_p;
   a.ws_out = ws_out;
-  a.stats_out = stats_out;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -427,8 +311,8 @@ hipError_t launch_scan(const Geo& g, const ScratchPtrs& sp, int64_t max_tokens,
     e = g.d == 128 ? launch_logits<false, 128>(a, units, st) : launch_logits<false, 64>(a, units, st);
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)(units * kDists)), dim3(256), 0, st, a);
-  return hipGetLastError();
+  FinishArgs f{g, sp, top_p, n_local, ws_out, stats_out};
+  return launch_finish(f, st);
 }
 
 }  // namespace gp

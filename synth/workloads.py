@@ -297,3 +297,32 @@ def direct_case(seed: int, B: int = 4, L: int = 2, Hq: int = 8, Hkv: int = 2, d:
     return Workload(name, L, Hq, Hkv, d, P, dtype, int(num_pages), int(max_pages), table, A, fill, pos,
                     rc, stack, top, k_rows, v_rows, sum_s.astype(np.float32), sum_l.astype(np.float32),
                     None, "f32", cos, sin, dict(params or PARAMS_DEFAULT), seed, regime=regime)
+
+
+def planted_logits_case(seed: int, logit_fns, L: int = 1, Hq: int = 8, Hkv: int = 2, d: int = 64,
+                        P: int = 16, params: Optional[dict] = None, spare_pages: int = 8,
+                        name: str = "planted") -> Workload:
+    """Requests whose scores are planted exactly: every summary (all heads, both
+    timescales) is the unit vector e_0 and key i carries logit_fn(rng, n)[i] * sqrt(d) in
+    component 0 (float32 storage, no RoPE), so each softmax row sees those logits.  Both
+    summaries coincide, so every request compacts.  ``logit_fns[b]`` = (n_alloc, fn)."""
+    rng = np.random.default_rng(seed)
+    B = len(logit_fns)
+    A = np.array([a for a, _ in logit_fns], np.int32)
+    fill = np.full(B, P, np.int32)
+    n = A * P + fill
+    num_pages = int(np.sum(A + 1)) + spare_pages
+    max_pages = int(A.max()) + 4
+    table, rc, stack, top = _pool_layout(rng, A, fill, P, num_pages, max_pages)
+    k_rows, v_rows = [], []
+    for b, (_, fn) in enumerate(logit_fns):
+        lg = np.asarray(fn(rng, int(n[b])), np.float64)
+        kb = rng.standard_normal((L, Hkv, int(n[b]), d))
+        kb[..., 0] = lg * math.sqrt(d)
+        k_rows.append(kb.astype(np.float32))
+        v_rows.append(rng.standard_normal((L, Hkv, int(n[b]), d)).astype(np.float32))
+    e0 = np.zeros((B, L, Hq, d), np.float32)
+    e0[..., 0] = 1.0
+    return Workload(name, L, Hq, Hkv, d, P, "f32", num_pages, max_pages, table, A, fill,
+                    n.astype(np.int32), rc, stack, top, k_rows, v_rows, e0, e0.copy(), None, "f32",
+                    None, None, dict(params or PARAMS_DEFAULT), seed, regime=np.zeros(B, np.int32))

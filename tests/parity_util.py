@@ -75,8 +75,10 @@ def compare_step(wl, slots, st, out, res: O.StepResult, n_local: int, check_page
             assert delta[b] == res.delta[b], (b, delta[b], res.delta[b])
         else:
             assert res.delta_lo[b] <= delta[b] <= res.delta_hi[b], (b, delta[b], res.delta_lo[b], res.delta_hi[b])
-    assert rep.decisions_ambiguous == 0, "seed gives an ambiguous decision; pick another"
-    assert np.array_equal(dec, res.decision), (dec, res.decision)
+    # An ambiguous decision (delta's near-tie range straddles tau) must still resolve like
+    # the oracle's for the rest of the batch to be comparable; planted cases with equal
+    # summaries resolve identically (delta is exactly 0 on both sides).
+    assert np.array_equal(dec, res.decision), (dec, res.decision, res.ambiguous)
     assert np.array_equal(status, res.status), (status, res.status)
 
     # ---- keep-sets

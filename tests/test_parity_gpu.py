@@ -171,3 +171,29 @@ def test_deterministic_repeat():
                      st.k_pool.view(torch.int16).cpu().numpy(), st.page_table.cpu().numpy()))
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+PLANTED = [
+    # every element in one bin, more than the LDS candidate buffer holds; equal importance
+    ("uniform_5k", [(312, lambda rng, n: np.zeros(n))], dict(SW.PARAMS_DEFAULT, n_local=0)),
+    # the mass crossing lies beyond the binned range (x > 255/16): whole-row fallback
+    ("tail_crossing", [(250, lambda rng, n: np.where(np.arange(n) < 2, 17.0, 0.0)[rng.permutation(n)])],
+     dict(SW.PARAMS_DEFAULT, top_p=0.99999, n_local=0)),
+    # importance falling with the slot: every new slot enters the keep buffer
+    ("falling", [(300, lambda rng, n: -np.arange(n) / 500.0)], dict(SW.PARAMS_DEFAULT, n_local=32)),
+    # importance rising with the slot: the oldest slots go
+    ("rising", [(200, lambda rng, n: np.arange(n) / 700.0)], dict(SW.PARAMS_DEFAULT, n_local=0)),
+    # narrow spread: thousands of elements inside the crossing bin
+    ("narrow", [(400, lambda rng, n: 0.02 * rng.standard_normal(n)),
+                (40, lambda rng, n: 3.0 * rng.standard_normal(n))], dict(SW.PARAMS_DEFAULT, n_local=16)),
+]
+
+
+@pytest.mark.parametrize("name,fns,params", PLANTED, ids=[c[0] for c in PLANTED])
+def test_planted_logits(name, fns, params):
+    wl = SW.planted_logits_case(zlib.crc32(name.encode()) % 10000, fns, params=params, name=name)
+    _say(f"[planted] {name} n={[wl.n(b) for b in range(wl.B)]}")
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, wl.params)
+    st, out, _ = run_step_gpu(wl)
+    rep = compare_step(wl, np.arange(wl.B), st, out, res, wl.params["n_local"])
+    _say(name, rep, res.counters, "W", res.W[:, 0, 0].tolist())
