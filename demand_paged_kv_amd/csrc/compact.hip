@@ -230,10 +230,30 @@ __global__ __launch_bounds__(256) void cowcopy_kernel(CompactArgs a) {
 }
 
 // ----------------------------------------------------------------------------- gather
-template <int NV>  // 16-byte vectors per thread per row part (a row is 4 parts)
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+constexpr int kPtLds = 2048;  // page-table entries of one request cached in LDS
+
+// Destination slot j receives source slot j + s(j) with s(j) = #{m : ev[m] - m <= j}
+// (ev ascending): the m-th evicted slot shifts every destination from ev[m] - m on.
+__device__ __forceinline__ int shift_of(const int* thr, int E, int j) {
+  int lo = 0, hi = E;  // first m with thr[m] > j
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (thr[mid] <= j) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// NV = 16-byte vectors per row / 4.  A step moves 64 destination rows; in each of its NV
+// load/store instructions the 256 threads cover 256/(4*NV) whole rows contiguously (lane t
+// takes 16-byte piece t % (4*NV) of a row), so every store writes complete cache lines.
+template <int NV>
 __global__ __launch_bounds__(256) void gather_kernel(CompactArgs a) {
   const Geo& g = a.g;
-  __shared__ int s_ev[256];
+  constexpr int CPR = 4 * NV;          // 16-byte pieces per row
+  constexpr int RPI = 256 / CPR;       // rows per instruction
+  __shared__ int s_thr[256];
+  __shared__ int s_pt[kPtLds];
   const int tid = threadIdx.x;
   int b, l, kvh;
   unit_of_block(g, a.sp, blockIdx.x, b, l, kvh);
@@ -242,44 +262,47 @@ __global__ __launch_bounds__(256) void gather_kernel(CompactArgs a) {
   const int r = g.req_ids[b];
   const int P = g.P;
   const int n = a.sp.n_tok[b];
-  const int k = g.n_alloc[r] * P;
+  const int A = g.n_alloc[r];
+  const int k = A * P;
   const int E = n - k;
   const int64_t u = ((int64_t)b * g.L + l) * g.Hkv + kvh;
   const int e = a.sp.e_unit[u];
   if (e >= k) return;
-  for (int i = tid; i < E; i += 256) s_ev[i] = a.sp.ev[u * P + i];
+  const int32_t* ptg = a.pg.page_table + (int64_t)r * g.max_pages;
+  const bool pt_lds = A + 1 <= kPtLds;
+  for (int i = tid; i < E; i += 256) s_thr[i] = a.sp.ev[u * P + i] - i;
+  if (pt_lds)
+    for (int i = tid; i <= A; i += 256) s_pt[i] = ptg[i];
   __syncthreads();
+  const int* pt = pt_lds ? s_pt : ptg;
   const int esz = g.dtype == GP_BF16 ? 2 : 4;
-  const int32_t* pt = a.pg.page_table + (int64_t)r * g.max_pages;
   const int64_t hoff = ((int64_t)l * g.s_layer + (int64_t)kvh * g.s_head) * esz;
   char* kb = reinterpret_cast<char*>(const_cast<void*>(g.k)) + hoff;
   char* vb = reinterpret_cast<char*>(const_cast<void*>(g.v)) + hoff;
-  const int part = tid & 3;
-  const int rr = tid >> 2;
-  const int64_t pbytes = (int64_t)NV * 16;
+  const int piece = (tid % CPR) * 16;
+  const int rr = tid / CPR;
+  const int64_t spage = g.s_page * esz, stok = g.s_tok * esz;
   for (int j0 = e; j0 < k; j0 += 64) {
-    const int jj = j0 + rr;
-    const bool act = jj < k;
-    uint4 kv[NV], vv[NV];
-    int64_t dsto = 0;
-    if (act) {
-      int s = 0;
-      for (int m = 0; m < E; ++m) s += (s_ev[m] <= jj + s) ? 1 : 0;
-      const int src = jj + s;
-      const int64_t srco = ((int64_t)pt[src / P] * g.s_page + (int64_t)(src % P) * g.s_tok) * esz + part * pbytes;
-      dsto = ((int64_t)pt[jj / P] * g.s_page + (int64_t)(jj % P) * g.s_tok) * esz + part * pbytes;
+    v4u kv[NV], vv[NV];
+    int64_t dsto[NV];
+    bool act[NV];
 #pragma unroll
-      for (int q = 0; q < NV; ++q) {
-        kv[q] = *reinterpret_cast<const uint4*>(kb + srco + q * 16);
-        vv[q] = *reinterpret_cast<const uint4*>(vb + srco + q * 16);
-      }
+    for (int q = 0; q < NV; ++q) {
+      const int jj = j0 + q * RPI + rr;
+      act[q] = jj < k;
+      const int jc = act[q] ? jj : k - 1;  // inactive lanes re-read a valid row, store nothing
+      const int src = jc + shift_of(s_thr, E, jc);
+      const int64_t srco = (int64_t)pt[src / P] * spage + (int64_t)(src % P) * stok + piece;
+      dsto[q] = (int64_t)pt[jc / P] * spage + (int64_t)(jc % P) * stok + piece;
+      kv[q] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(kb + srco));
+      vv[q] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(vb + srco));
     }
-    __syncthreads();
-    if (act) {
+    __syncthreads();  // every read of this step lands before any write of it
 #pragma unroll
-      for (int q = 0; q < NV; ++q) {
-        *reinterpret_cast<uint4*>(kb + dsto + q * 16) = kv[q];
-        *reinterpret_cast<uint4*>(vb + dsto + q * 16) = vv[q];
+    for (int q = 0; q < NV; ++q) {
+      if (act[q]) {
+        __builtin_nontemporal_store(kv[q], reinterpret_cast<v4u*>(kb + dsto[q]));
+        __builtin_nontemporal_store(vv[q], reinterpret_cast<v4u*>(vb + dsto[q]));
       }
     }
   }
