@@ -22,7 +22,8 @@ COUNTER_NAMES = ("grows", "compacts", "grow_denied", "deferred", "cow_pages", "f
                  "moved_rows", "copied_rows")
 GP_NUM_COUNTERS = len(COUNTER_NAMES)
 
-EXPORTED = ("gp_abi_version", "gp_status_string", "gp_update_summaries", "gp_scratch_bytes",
+EXPORTED = ("gp_abi_version", "gp_status_string", "gp_last_hip_error_string", "gp_update_summaries",
+            "gp_scratch_bytes",
             "gp_boundary_scan", "gp_decide", "gp_compact", "gp_compact_prepare", "gp_compact_move",
             "gp_append_kv")
 
@@ -61,12 +62,17 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise GrowPageError(f"{path} not found: build it with `python -m demand_paged_kv_amd.build`")
+    # torch ships its own HIP runtime; load it first so that the library binds to the same
+    # runtime (one HIP runtime per process), otherwise torch's streams and pointers would
+    # be foreign to the runtime the library launches on.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.gp_abi_version.restype = i32
     lib.gp_status_string.restype = ctypes.c_char_p
     lib.gp_status_string.argtypes = [i32]
+    lib.gp_last_hip_error_string.restype = ctypes.c_char_p
     lib.gp_update_summaries.restype = i32
     lib.gp_update_summaries.argtypes = [P, i32, i64, i64, i64, P, i32, i32, i32, i32, P, P,
                                         ctypes.POINTER(Params), P]
@@ -112,7 +118,10 @@ def _stream(stream) -> Optional[int]:
 
 def _check(status: int, what: str):
     if status != GP_OK:
-        msg = load().gp_status_string(status).decode()
+        lib = load()
+        msg = lib.gp_status_string(status).decode()
+        if status == GP_ERR_HIP:
+            msg += f" ({lib.gp_last_hip_error_string().decode()})"
         raise GrowPageError(f"{what}: {msg}")
 
 

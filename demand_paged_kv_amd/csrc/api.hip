@@ -10,7 +10,13 @@ namespace {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-gp_status from_hip(hipError_t e) { return e == hipSuccess ? GP_OK : GP_ERR_HIP; }
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+gp_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return GP_OK;
+  g_last_hip_error = e;
+  return GP_ERR_HIP;
+}
 
 gp_status check_params(const gp_params* p) {
   if (!p) return GP_ERR_INVALID;
@@ -75,6 +81,8 @@ Geo make_geo(const gp_kv* kv, const gp_pages* pg, const int32_t* req_ids, int32_
 extern "C" {
 
 int32_t gp_abi_version(void) { return GP_ABI_VERSION; }
+
+const char* gp_last_hip_error_string(void) { return hipGetErrorString(g_last_hip_error); }
 
 const char* gp_status_string(int32_t status) {
   switch (status) {

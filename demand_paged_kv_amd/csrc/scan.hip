@@ -175,12 +175,38 @@ __device__ __forceinline__ void unpack_chunk(const Chunk<BF16, D>& c, float* kf)
 // summary and lane j finishes with summary j.
 __device__ __forceinline__ int slot_dist(int j, int i) { return i < 4 ? (j ^ i) : (j ^ 7 ^ (i - 4)); }
 
+constexpr int kPtCache = 4096;  // page-table entries of one request cached in LDS
+
+// One step = 8 tokens of one page.  Accumulate the 8 scores of this lane's token slice
+// and transpose-reduce them so that lane j of each 8-lane group holds summary j.
+template <bool BF16, int D>
+__device__ __forceinline__ float step_scores(const Chunk<BF16, D>& c, const float (&qr)[8][D / 8]) {
+  constexpr int W = D / 16;
+  float kf[2 * W];
+  unpack_chunk<BF16, D>(c, kf);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 2 * W; ++e) s = __builtin_fmaf(qr[i][e], kf[e], s);
+    acc[i] = s;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] += dpp_mov<kDppHalfMirror>(acc[i + 4]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) acc[i] += dpp_mov<kDppQuadXor2>(acc[i + 2]);
+  acc[0] += dpp_mov<kDppQuadXor1>(acc[1]);
+  return acc[0];
+}
+
 template <bool BF16, int D>
 __global__ __launch_bounds__(64) void logit_kernel(ScanArgs a) {
 #pragma clang fp contract(off)
   constexpr int W = D / 16;
-  constexpr int U = 4;  // token steps per load batch
+  constexpr int U = 4;  // steps per batch of loads
   constexpr int E = BF16 ? 2 : 4;
+  __shared__ int s_pt[kPtCache];
   const Geo& g = a.g;
   const int lane = threadIdx.x;
   const int tl = lane >> 3;
@@ -194,12 +220,22 @@ __global__ __launch_bounds__(64) void logit_kernel(ScanArgs a) {
   if (a.sp.flags[b]) return;
   const int n = a.sp.n_tok[b];
   const int r = g.req_ids[b];
+  const int32_t* ptg = g.page_table + (int64_t)r * g.max_pages;
+  const int npages = (n + g.P - 1) / g.P;
+  const bool cached = npages <= kPtCache;
+  if (cached)
+    for (int i = lane; i < npages; i += 64) s_pt[i] = ptg[i];
 
   // Rotate the 8 summaries to the request position and fold in 1/sqrt(d).
   float qr[8][2 * W];
   const bool rope = a.rope_cos != nullptr;
-  int pos = 0;
-  if (rope) pos = min(max(a.pos[r], 0), a.rope_max_pos - 1);
+  const int pos = rope ? min(max(a.pos[r], 0), a.rope_max_pos - 1) : 0;
+  float cs[W], sn[W];
+#pragma unroll
+  for (int e = 0; e < W; ++e) {
+    cs[e] = rope ? a.rope_cos[(int64_t)pos * (D / 2) + j * W + e] : 1.f;
+    sn[e] = rope ? a.rope_sin[(int64_t)pos * (D / 2) + j * W + e] : 0.f;
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int dist = slot_dist(j, i);
@@ -209,61 +245,64 @@ __global__ __launch_bounds__(64) void logit_kernel(ScanArgs a) {
     for (int e = 0; e < W; ++e) {
       const float x1 = s[j * W + e];
       const float x2 = s[D / 2 + j * W + e];
-      if (rope) {
-        const float c = a.rope_cos[(int64_t)pos * (D / 2) + j * W + e];
-        const float sn = a.rope_sin[(int64_t)pos * (D / 2) + j * W + e];
-        qr[i][e] = (x1 * c - x2 * sn) * a.scale;
-        qr[i][W + e] = (x2 * c + x1 * sn) * a.scale;
-      } else {
-        qr[i][e] = x1 * a.scale;
-        qr[i][W + e] = x2 * a.scale;
-      }
+      qr[i][e] = (x1 * cs[e] - x2 * sn[e]) * a.scale;
+      qr[i][W + e] = (x2 * cs[e] + x1 * sn[e]) * a.scale;
     }
   }
+  __syncthreads();
+  const int* pt = cached ? s_pt : ptg;
 
   const int64_t unit_base =
       (a.sp.tok_off[b] * g.L * g.Hkv + (int64_t)(l * g.Hkv + kvh) * n) * kDists;
-  float* lg = a.sp.logits + unit_base + j;  // token-major: [n][8]
-  const char* kb = reinterpret_cast<const char*>(g.k) + ((int64_t)l * g.s_layer + (int64_t)kvh * g.s_head) * E;
-  const int32_t* pt = g.page_table + (int64_t)r * g.max_pages;
+  float* lg = a.sp.logits + unit_base + j + tl * kDists;  // token-major: [n][8]
+  const char* kb = reinterpret_cast<const char*>(g.k) + ((int64_t)l * g.s_layer + (int64_t)kvh * g.s_head) * E +
+                   (int64_t)tl * g.s_tok * E;
+  const int64_t page_bytes = g.s_page * E;
+  const int64_t tok_bytes = g.s_tok * E;
   float m = -INFINITY;
 
-  for (int t0 = 0; t0 < n; t0 += 8 * U) {
-    Chunk<BF16, D> raw[U] = {};
+  // Full batches of U steps, loads of the next batch issued before this one is reduced.
+  const int nfull = (n / (8 * U)) * (8 * U);
+  int pj = 0, sub = 0;  // page index and in-page offset of the next step to load
+  auto load_batch = [&](Chunk<BF16, D>(&c)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int ts = t0 + u * 8;
-      if (ts < n) {
-        const int page = pt[ts / g.P];
-        const int slot = (ts % g.P) + tl;
-        const char* row = kb + ((int64_t)page * g.s_page + (int64_t)slot * g.s_tok) * E;
-        if (ts + tl < n) load_chunk<BF16, D>(raw[u], row, j);
+      const char* row = kb + (int64_t)pt[pj] * page_bytes + (int64_t)sub * tok_bytes;
+      load_chunk<BF16, D>(c[u], row, j);
+      sub += 8;
+      if (sub == g.P) {
+        sub = 0;
+        ++pj;
       }
     }
+  };
+  Chunk<BF16, D> cur[U], nxt[U];
+  if (nfull > 0) load_batch(cur);
+  for (int t0 = 0; t0 < nfull; t0 += 8 * U) {
+    if (t0 + 8 * U < nfull) load_batch(nxt);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int ts = t0 + u * 8;
-      if (ts >= n) break;
-      float kf[2 * W];
-      unpack_chunk<BF16, D>(raw[u], kf);
-      float acc[8];
+      const float x = step_scores<BF16, D>(cur[u], qr);
+      lg[(int64_t)(t0 + 8 * u) * kDists] = x;
+      m = fmaxf(m, x);
+    }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < 2 * W; ++e) s = __builtin_fmaf(qr[i][e], kf[e], s);
-        acc[i] = s;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += dpp_mov<kDppHalfMirror>(acc[i + 4]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) acc[i] += dpp_mov<kDppQuadXor2>(acc[i + 2]);
-      acc[0] += dpp_mov<kDppQuadXor1>(acc[1]);
-      const int tok = ts + tl;
-      if (tok < n) {
-        lg[(int64_t)tok * kDists] = acc[0];
-        m = fmaxf(m, acc[0]);
-      }
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+  }
+  // Tail: single steps, the last one possibly partial.
+  for (int t0 = nfull; t0 < n; t0 += 8) {
+    Chunk<BF16, D> c{};
+    const bool ok = t0 + tl < n;
+    if (ok) load_chunk<BF16, D>(c, kb + (int64_t)pt[pj] * page_bytes + (int64_t)sub * tok_bytes, j);
+    sub += 8;
+    if (sub == g.P) {
+      sub = 0;
+      ++pj;
+    }
+    const float x = step_scores<BF16, D>(c, qr);
+    if (ok) {
+      lg[(int64_t)t0 * kDists] = x;
+      m = fmaxf(m, x);
     }
   }
   m = fmaxf(m, __shfl_xor(m, 8, 64));

@@ -124,6 +124,10 @@ int32_t gp_abi_version(void);
 /* Human-readable name of a gp_status value (static string). */
 const char* gp_status_string(int32_t status);
 
+/* Text of the HIP error behind the calling thread's most recent GP_ERR_HIP (static
+ * string from the HIP runtime; "no error" if there was none). */
+const char* gp_last_hip_error_string(void);
+
 /* Summary update, for every batch entry b, layer l, query head h and element i:
  *   S <- beta_s*S + (1-beta_s)*q,   L <- beta_l*L + (1-beta_l)*q
  * in float32 with each product and the sum rounded separately and (1-beta) formed in

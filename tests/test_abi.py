@@ -96,3 +96,15 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert lib.gp_update_summaries(0x1000, 1, 4, 4, 6, 0x2000, 1, 2, 8, 64, 0x3000, 0x4000, P(prm), None) == B.GP_ERR_INVALID
     assert lib.gp_update_summaries(0x1000, 1, 4, 4, 4, 0x2000, 0, 2, 8, 64, 0x3000, 0x4000, P(prm), None) == B.GP_OK
     assert lib.gp_append_kv(P(kv), P(pg), None, 0x10, 0x9000, 1, None, None) == B.GP_ERR_INVALID
+
+
+def test_single_hip_runtime_after_load():
+    """Loading the library through the binding leaves exactly one HIP runtime in the process
+    (torch's), whatever was imported before."""
+    import subprocess
+    import sys
+    code = ("import demand_paged_kv_amd.binding as B; B.load(); import torch; "
+            "print(len({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"
