@@ -14,9 +14,10 @@
 //   cowassign_kernel per entry: assign popped pages in ascending page index, rewrite the
 //                    page table, record (old, new).
 //   cowcopy_kernel   copy every (old page, layer, KV head) block of K and V to the new page.
-//   gather_kernel    per unit: in-place stable compaction, slot j <- slot kept[j] for
-//                    j in [e, k), 64 destination rows per step, all reads of a step
-//                    before its writes (destinations never exceed sources).
+//   gather_kernel    per unit and tensor (K blocks first, then V blocks): in-place stable
+//                    compaction, slot j <- slot kept[j] for j in [e, k), 128 destination
+//                    rows per step, all reads of a step before its writes (destinations
+//                    never exceed sources).
 //   finalize_kernel  1 block: refcount decrements of replaced pages, push the pages that
 //                    reached zero in ascending id order, empty the write pages, counters.
 #include "device_util.h"
@@ -244,19 +245,25 @@ __device__ __forceinline__ int shift_of(const int* thr, int E, int j) {
   return lo;
 }
 
-// NV = 16-byte vectors per row / 4.  A step moves 64 destination rows; in each of its NV
-// load/store instructions the 256 threads cover 256/(4*NV) whole rows contiguously (lane t
-// takes 16-byte piece t % (4*NV) of a row), so every store writes complete cache lines.
-template <int NV>
+// One block moves the rows of one tensor (K or V) of one unit; all K blocks come before
+// all V blocks in the grid, so the two tensors are never walked in lockstep (identical
+// in-pool offsets of K and V would otherwise hit the same HBM channels together).  A
+// step moves 128 destination rows; in each of its load/store instructions the 256
+// threads cover 256/CPR whole rows contiguously (lane t takes 16-byte piece t % CPR of a
+// row), so every store writes complete cache lines.
+template <int CPR>  // 16-byte pieces per row
 __global__ __launch_bounds__(256) void gather_kernel(CompactArgs a) {
   const Geo& g = a.g;
-  constexpr int CPR = 4 * NV;          // 16-byte pieces per row
+  constexpr int ROWS = 128;            // destination rows per step
   constexpr int RPI = 256 / CPR;       // rows per instruction
+  constexpr int NI = ROWS / RPI;       // instructions per step
   __shared__ int s_thr[256];
   __shared__ int s_pt[kPtLds];
   const int tid = threadIdx.x;
+  const int units = g.n_req * g.L * g.Hkv;
+  const int which = blockIdx.x >= units ? 1 : 0;
   int b, l, kvh;
-  unit_of_block(g, a.sp, blockIdx.x, b, l, kvh);
+  unit_of_block(g, a.sp, blockIdx.x - which * units, b, l, kvh);
   const int32_t* rq = a.sp.req + (int64_t)b * RQ_N;
   if (rq[RQ_STATE] != ST_GO) return;
   const int r = g.req_ids[b];
@@ -277,34 +284,28 @@ __global__ __launch_bounds__(256) void gather_kernel(CompactArgs a) {
   const int* pt = pt_lds ? s_pt : ptg;
   const int esz = g.dtype == GP_BF16 ? 2 : 4;
   const int64_t hoff = ((int64_t)l * g.s_layer + (int64_t)kvh * g.s_head) * esz;
-  char* kb = reinterpret_cast<char*>(const_cast<void*>(g.k)) + hoff;
-  char* vb = reinterpret_cast<char*>(const_cast<void*>(g.v)) + hoff;
+  char* base = reinterpret_cast<char*>(const_cast<void*>(which ? g.v : g.k)) + hoff;
   const int piece = (tid % CPR) * 16;
   const int rr = tid / CPR;
   const int64_t spage = g.s_page * esz, stok = g.s_tok * esz;
-  for (int j0 = e; j0 < k; j0 += 64) {
-    v4u kv[NV], vv[NV];
-    int64_t dsto[NV];
-    bool act[NV];
+  for (int j0 = e; j0 < k; j0 += ROWS) {
+    v4u val[NI];
+    int64_t dsto[NI];
+    bool act[NI];
 #pragma unroll
-    for (int q = 0; q < NV; ++q) {
+    for (int q = 0; q < NI; ++q) {
       const int jj = j0 + q * RPI + rr;
       act[q] = jj < k;
       const int jc = act[q] ? jj : k - 1;  // inactive lanes re-read a valid row, store nothing
       const int src = jc + shift_of(s_thr, E, jc);
       const int64_t srco = (int64_t)pt[src / P] * spage + (int64_t)(src % P) * stok + piece;
       dsto[q] = (int64_t)pt[jc / P] * spage + (int64_t)(jc % P) * stok + piece;
-      kv[q] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(kb + srco));
-      vv[q] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(vb + srco));
+      val[q] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(base + srco));
     }
     __syncthreads();  // every read of this step lands before any write of it
 #pragma unroll
-    for (int q = 0; q < NV; ++q) {
-      if (act[q]) {
-        __builtin_nontemporal_store(kv[q], reinterpret_cast<v4u*>(kb + dsto[q]));
-        __builtin_nontemporal_store(vv[q], reinterpret_cast<v4u*>(vb + dsto[q]));
-      }
-    }
+    for (int q = 0; q < NI; ++q)
+      if (act[q]) __builtin_nontemporal_store(val[q], reinterpret_cast<v4u*>(base + dsto[q]));
   }
 }
 
@@ -435,13 +436,14 @@ hipError_t launch_compact_move(const Geo& g, const gp_pages& pg, const ScratchPt
   CompactArgs a{g, pg, sp, nullptr, 0, nullptr, nullptr, counters_out};
   const unsigned units = (unsigned)((int64_t)g.n_req * g.L * g.Hkv);
   const int esz = g.dtype == GP_BF16 ? 2 : 4;
-  const int nv = g.d * esz / 64;  // 16-byte vectors per quarter row
-  if (nv == 2)
-    hipLaunchKernelGGL(gather_kernel<2>, dim3(units), dim3(256), 0, st, a);
-  else if (nv == 4)
-    hipLaunchKernelGGL(gather_kernel<4>, dim3(units), dim3(256), 0, st, a);
+  const int cpr = g.d * esz / 16;  // 16-byte pieces per row: 8, 16 or 32
+  const dim3 grid(2 * units);      // K blocks, then V blocks
+  if (cpr == 8)
+    hipLaunchKernelGGL(gather_kernel<8>, grid, dim3(256), 0, st, a);
+  else if (cpr == 16)
+    hipLaunchKernelGGL(gather_kernel<16>, grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(gather_kernel<8>, dim3(units), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(gather_kernel<32>, grid, dim3(256), 0, st, a);
   hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1024), 0, st, a);
   return hipGetLastError();
 }

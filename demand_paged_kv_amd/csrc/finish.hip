@@ -4,27 +4,27 @@
 // FAQ "Is GrowPage's code available?": local retention quota.)
 //
 // One 256-thread block per (entry, layer, KV head) unit, two reads of the unit's logits
-// ([n][8] float32, token-major, written by the logit kernel with each row's max M; a
-// thread loads a token's 8 logits as two 16-byte vectors, two tokens at a time):
+// ([n][8] float32, token-major, written by the logit kernel with each row's max M):
 //
-//   read 1  x = M - l >= 0 for every element of every row; elements with x < 255/16 go
-//           to 255 bins of width 1/16 (count + softmax mass exp(-x) in 2^-40 fixed
-//           point, LDS atomics), the rest only add their mass to a per-thread tail sum.
-//           Integer sums make the normaliser Z exact and order-independent.  Bins are
-//           walked from x = 0 (largest probabilities) until the mass reaches
-//           T = ceil(top_p * Z): that bin holds the W-th element.
-//   read 2  the elements of each row's crossing bin are gathered into LDS; in the same
+//   read 1  x = M - l >= 0 for every element of the 8 rows.  Elements with x < 255/16
+//           add their softmax mass exp(-x) (2^-40 fixed point, one 64-bit LDS atomic)
+//           to one of 255 bins of width 1/16; the rest add it to a per-thread tail sum.
+//           Integer sums make the normaliser Z exact and order-independent.  Walking
+//           the bins from x = 0 (largest probabilities) gives the bin b* where the mass
+//           reaches T = ceil(top_p * Z) -- or the tail, if the bins never reach it.
+//   read 2  per row: elements above b* are counted in registers, the elements of b* are
+//           appended to an LDS buffer (its size is bounded from the bin's mass: every
+//           element of bin b carries at least the mass of x = (b+1)/16); in the same
 //           pass the slot importance max_k exp(l_k - M_k) / Z_k feeds a threshold
 //           buffer that keeps the n - k least important candidate slots (ties: older
-//           slot first), i.e. the slots a compaction evicts.
-//   refine  per row, an exact radix select over the crossing-bin elements only (one
-//           wave per row), weighted by the same fixed-point masses, gives
-//           W = (elements above the bin) + (elements of the bin needed to reach T).
-//
-// A crossing beyond the binned range (possible only when the W-th probability is below
-// exp(-255/16), i.e. inside the near-tie band) or a crossing bin larger than the LDS
-// candidate buffer falls back to the same radix select over the whole row in global
-// memory.  All decisions are exact for the float32 logits the scan produced.
+//           slot first) -- the slots a compaction evicts.
+//   refine  per row, an exact radix select over the b* elements only, weighted by the
+//           same fixed-point masses, starting at the highest key bit in which they
+//           differ: W = (elements above b*) + (elements of b* needed to reach T).
+//           Rows whose b* elements did not fit the buffer (or whose crossing lies in the
+//           tail, which only a near-tie allows) are refined by the whole block from
+//           the logits in global memory, filtered to b*.
+// All decisions are exact for the float32 logits the scan produced.
 #include "device_util.h"
 #include "gp_internal.h"
 
@@ -33,16 +33,24 @@ namespace {
 
 typedef unsigned long long u64;
 
-constexpr int kXBins = 255;          // bins of width 1/16 covering x in [0, 255/16)
+constexpr int kXBins = 255;          // bins of width 1/16 covering x in [0, 255/16); 255 = tail
 constexpr float kBinsPerNat = 16.0f;
-constexpr int kCandCap = 4096;       // crossing-bin elements held in LDS (all 8 rows)
+constexpr int kCandCap = 6144;       // crossing-bin elements held in LDS (all 8 rows)
 constexpr int kKeepCap = 512;        // threshold buffer of keep-set candidates
 
 enum { MODE_DONE = 0, MODE_LDS = 1, MODE_GLOBAL = 2 };
 
 __device__ __forceinline__ int x_bin(float xv) {
   const float f = xv * kBinsPerNat;
-  return f < (float)kXBins ? (int)f : kXBins;  // kXBins = beyond the bins
+  return f < (float)kXBins ? (int)f : kXBins;
+}
+
+// Order the LDS accesses of one wave without a block barrier.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __device__ __forceinline__ u64 wave_exscan_u64(u64 v, int lane, u64* total) {
@@ -66,14 +74,25 @@ __device__ __forceinline__ uint32_t wave_exscan_u32(uint32_t v, int lane) {
   return x - v;
 }
 
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
 // Walk 256 bins (lane l owns 4 consecutive bins in walk order; DESC walks bin 255 first)
-// accumulating mass from (base_mass, base_cnt) and return the first bin where the
-// accumulated mass reaches T, with the mass and count strictly before it.
+// accumulating mass from (base_mass, base_cnt); return the first bin where the mass
+// reaches T together with the mass and count strictly before it.  cnt may be null
+// (counts then stay at base_cnt).
 template <bool DESC>
 __device__ __forceinline__ bool wave_find_crossing(const uint32_t* cnt, const u64* ms, u64 base_mass,
                                                    uint32_t base_cnt, u64 T, int lane, int* chosen,
-                                                   u64* mass_before, uint32_t* cnt_before,
-                                                   u64* total_mass) {
+                                                   u64* mass_before, uint32_t* cnt_before) {
   u64 m4[4];
   uint32_t c4[4];
   u64 ls = 0;
@@ -82,21 +101,20 @@ __device__ __forceinline__ bool wave_find_crossing(const uint32_t* cnt, const u6
   for (int q = 0; q < 4; ++q) {
     const int bin = DESC ? 255 - (4 * lane + q) : 4 * lane + q;
     m4[q] = ms[bin];
-    c4[q] = cnt[bin];
+    c4[q] = cnt ? cnt[bin] : 0u;
     ls += m4[q];
     lc += c4[q];
   }
   u64 tot = 0;
   u64 acc = base_mass + wave_exscan_u64(ls, lane, &tot);
   uint32_t ac = base_cnt + wave_exscan_u32(lc, lane);
-  *total_mass = tot;
   int my = -1;
   u64 my_m = 0;
   uint32_t my_c = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     if (my < 0) {
-      if (c4[q] > 0 && acc + m4[q] >= T) {
+      if (m4[q] > 0 && acc + m4[q] >= T) {
         my = DESC ? 255 - (4 * lane + q) : 4 * lane + q;
         my_m = acc;
         my_c = ac;
@@ -115,56 +133,128 @@ __device__ __forceinline__ bool wave_find_crossing(const uint32_t* cnt, const u6
   return true;
 }
 
-// Exact weighted radix select run by one wave over m logits of one row: keys descending,
-// (acc_cnt, acc_mass) already hold the elements above the range.  All four waves of the
-// block call it the same number of times (inactive waves pass active = false) because it
-// synchronises the block between passes.  Returns W on lane 0's view (uniform).
-__device__ int wave_radix_refine(bool active, const float* src, int stride, int m, float M, u64 T,
-                                 u64 acc_mass, uint32_t acc_cnt, uint32_t* hcnt, u64* hms, int lane,
-                                 int n) {
-  uint32_t prefix = 0, mask = 0;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    if (active)
-      for (int q = lane; q < 256; q += 64) {
-        hcnt[q] = 0;
-        hms[q] = 0;
-      }
-    __syncthreads();
-    if (active)
-      for (int c = lane; c < m; c += 64) {
-        const float v = src[(int64_t)c * stride];
-        const uint32_t key = ord_key(v);
-        if ((key & mask) == prefix) {
-          const uint32_t bin = (key >> shift) & 255u;
-          atomicAdd(&hcnt[bin], 1u);
-          atomicAdd(&hms[bin], (u64)fixed_mass(v - M));
-        }
-      }
-    __syncthreads();
-    if (active) {
-      int chosen = 0;
-      u64 mb = acc_mass, tot = 0;
-      uint32_t cb = acc_cnt;
-      if (wave_find_crossing<true>(hcnt, hms, acc_mass, acc_cnt, T, lane, &chosen, &mb, &cb, &tot)) {
-        acc_mass = mb;
-        acc_cnt = cb;
-        prefix |= (uint32_t)chosen << shift;
-        mask |= 255u << shift;
-      } else {
-        // unreachable when T <= the range mass; keep the widest answer
-        prefix |= 0u;
-        mask |= 255u << shift;
-      }
-    }
-    __syncthreads();
-  }
-  if (!active) return 0;
+// W from the final key: (above) + elements of value vstar needed to reach T.
+__device__ __forceinline__ int finish_w(uint32_t prefix, float M, u64 T, u64 acc_mass, uint32_t acc_cnt,
+                                        int n) {
   const float vstar = ord_key_inv(prefix);
   const u64 q = fixed_mass(vstar - M);
   const u64 need = T > acc_mass ? T - acc_mass : 0;
   const u64 jn = q ? (need + q - 1) / q : 1ull;
   return (int)min((u64)n, (u64)acc_cnt + max(jn, 1ull));
+}
+
+// Exact weighted radix select by one wave over the m LDS elements of one row (keys
+// descending), synchronised within the wave only.  (acc_cnt, acc_mass) hold the
+// elements above the range.  Radix digits start at the highest differing key bit.
+__device__ int wave_refine_lds(const float* src, int m, float M, u64 T, u64 acc_mass, uint32_t acc_cnt,
+                               uint32_t* hcnt, u64* hms, int lane, int n) {
+  uint32_t kmin = 0xffffffffu, kmax = 0;
+  for (int c = lane; c < m; c += 64) {
+    const uint32_t key = ord_key(src[c]);
+    kmin = min(kmin, key);
+    kmax = max(kmax, key);
+  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (kmin == kmax) return finish_w(kmin, M, T, acc_mass, acc_cnt, n);
+  const int hb = 31 - __builtin_clz(kmin ^ kmax);     // highest differing bit
+  uint32_t mask = hb >= 31 ? 0u : ~((2u << hb) - 1u);  // bits above hb: common to all
+  uint32_t prefix = kmin & mask;
+  for (int shift = (hb / 8) * 8; shift >= 0; shift -= 8) {
+    for (int q = lane; q < 256; q += 64) {
+      hcnt[q] = 0;
+      hms[q] = 0;
+    }
+    wave_lds_sync();
+    for (int c = lane; c < m; c += 64) {
+      const float v = src[c];
+      const uint32_t key = ord_key(v);
+      if ((key & mask) == prefix) {
+        const uint32_t bin = (key >> shift) & 255u;
+        atomicAdd(&hcnt[bin], 1u);
+        atomicAdd(&hms[bin], (u64)fixed_mass(v - M));
+      }
+    }
+    wave_lds_sync();
+    int chosen = 0;
+    u64 mb = acc_mass;
+    uint32_t cb = acc_cnt;
+    if (wave_find_crossing<true>(hcnt, hms, acc_mass, acc_cnt, T, lane, &chosen, &mb, &cb)) {
+      acc_mass = mb;
+      acc_cnt = cb;
+      prefix |= (uint32_t)chosen << shift;
+    }
+    mask |= 255u << shift;
+    wave_lds_sync();
+  }
+  return finish_w(prefix, M, T, acc_mass, acc_cnt, n);
+}
+
+// The same select by the whole block over the elements of one row in global memory whose
+// bin is `bstar` (token-major logits, stride 8).  Block-uniform control flow.
+__device__ int block_refine_global(const float* row, int n, int bstar, float M, u64 T, u64 acc_mass,
+                                   uint32_t acc_cnt, uint32_t* hcnt, u64* hms, uint32_t* red, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  uint32_t kmin = 0xffffffffu, kmax = 0;
+  for (int i = tid; i < n; i += 256) {
+    const float v = row[(int64_t)i * kDists];
+    if (x_bin(M - v) == bstar) {
+      const uint32_t key = ord_key(v);
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
+    }
+  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) {
+    red[wave] = kmin;
+    red[4 + wave] = kmax;
+  }
+  __syncthreads();
+  kmin = min(min(red[0], red[1]), min(red[2], red[3]));
+  kmax = max(max(red[4], red[5]), max(red[6], red[7]));
+  __syncthreads();
+  if (kmin == kmax) return finish_w(kmin, M, T, acc_mass, acc_cnt, n);
+  const int hb = 31 - __builtin_clz(kmin ^ kmax);
+  uint32_t mask = hb >= 31 ? 0u : ~((2u << hb) - 1u);
+  uint32_t prefix = kmin & mask;
+  for (int shift = (hb / 8) * 8; shift >= 0; shift -= 8) {
+    hcnt[tid] = 0;
+    hms[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) {
+      const float v = row[(int64_t)i * kDists];
+      const uint32_t key = ord_key(v);
+      if (x_bin(M - v) == bstar && (key & mask) == prefix) {
+        const uint32_t bin = (key >> shift) & 255u;
+        atomicAdd(&hcnt[bin], 1u);
+        atomicAdd(&hms[bin], (u64)fixed_mass(v - M));
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int chosen = 0;
+      u64 mb = acc_mass;
+      uint32_t cb = acc_cnt;
+      const bool ok = wave_find_crossing<true>(hcnt, hms, acc_mass, acc_cnt, T, lane, &chosen, &mb, &cb);
+      if (lane == 0) {
+        red[0] = ok ? 1u : 0u;
+        red[1] = (uint32_t)chosen;
+        red[2] = cb;
+        red[3] = (uint32_t)(mb & 0xffffffffu);
+        red[4] = (uint32_t)(mb >> 32);
+      }
+    }
+    __syncthreads();
+    if (red[0]) {
+      prefix |= red[1] << shift;
+      acc_cnt = red[2];
+      acc_mass = ((u64)red[4] << 32) | red[3];
+    }
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+  return finish_w(prefix, M, T, acc_mass, acc_cnt, n);
 }
 
 __device__ void bitonic_sort_512(u64* a, int tid) {
@@ -185,14 +275,13 @@ __device__ void bitonic_sort_512(u64* a, int tid) {
 
 __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
   const Geo& g = a.g;
-  __shared__ uint32_t cnt[kDists][256];
-  __shared__ u64 ms[kDists][256];
+  __shared__ u64 ms[kDists][256];          // read 1 bins; later refinement histograms
   __shared__ float cand[kCandCap];
   __shared__ u64 kbuf[kKeepCap];
   __shared__ float s_M[kDists], s_iz[kDists];
   __shared__ u64 s_tail[kDists], s_T[kDists], s_above[kDists], s_Z[kDists];
-  __shared__ uint32_t s_above_cnt[kDists];
-  __shared__ int s_mode[kDists], s_bin[kDists], s_off[kDists], s_cn[kDists], s_fill[kDists], s_W[kDists];
+  __shared__ uint32_t s_above_cnt[kDists], s_red[8];
+  __shared__ int s_mode[kDists], s_bin[kDists], s_off[kDists], s_fill[kDists], s_ub[kDists], s_W[kDists];
   __shared__ int s_kcount;
   __shared__ u64 s_ktau;
 
@@ -233,14 +322,12 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
     return;
   }
 
-  // ---- read 1: x-bins and the tail mass
-  for (int i = tid; i < kDists * 256; i += 256) {
-    (&cnt[0][0])[i] = 0;
-    (&ms[0][0])[i] = 0;
-  }
+  // ---- read 1: binned masses and the tail mass
+  for (int i = tid; i < kDists * 256; i += 256) (&ms[0][0])[i] = 0;
   if (tid < kDists) {
     s_M[tid] = a.sp.stats[widx(tid) * 2];
     s_tail[tid] = 0;
+    s_above_cnt[tid] = 0;
   }
   __syncthreads();
   float M[kDists];
@@ -270,12 +357,10 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
         const float xv = M[k] - v[t][k];
         const u64 q = fixed_mass(-xv);
         const int bin = x_bin(xv);
-        if (bin < kXBins) {
-          atomicAdd(&cnt[k][bin], 1u);
+        if (bin < kXBins)
           atomicAdd(&ms[k][bin], q);
-        } else {
+        else
           tail[k] += q;
-        }
       }
     }
   }
@@ -291,10 +376,6 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
   // ---- crossing bin of each row (wave w: rows 2w, 2w+1)
   for (int d2 = 0; d2 < 2; ++d2) {
     const int k = 2 * wave + d2;
-    int chosen = 0;
-    u64 mb = 0, tot = 0;
-    uint32_t cb = 0;
-    // total first (T depends on it)
     u64 ls = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) ls += ms[k][4 * lane + q];
@@ -302,7 +383,9 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
     wave_exscan_u64(ls, lane, &tot_bins);
     const u64 Z = tot_bins + s_tail[k];
     u64 T = 0;
-    int mode = MODE_LDS, W = 0;
+    int mode = MODE_LDS, W = 0, chosen = kXBins;
+    u64 mb = tot_bins;
+    uint32_t cb = 0;
     if (a.top_p >= 1.0f) {
       mode = MODE_DONE;
       W = n;
@@ -313,30 +396,41 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
         W = 1;
       }
     }
-    bool found = false;
-    if (mode == MODE_LDS)
-      found = wave_find_crossing<false>(&cnt[k][0], &ms[k][0], 0, 0, T, lane, &chosen, &mb, &cb, &tot);
+    if (mode == MODE_LDS && !wave_find_crossing<false>(nullptr, &ms[k][0], 0, 0, T, lane, &chosen, &mb, &cb)) {
+      chosen = kXBins;  // crossing in the tail: every bin lies above it
+      mb = tot_bins;
+      mode = MODE_GLOBAL;
+    }
     if (lane == 0) {
-      if (mode == MODE_LDS && !found) mode = MODE_GLOBAL;
       s_mode[k] = mode;
       s_W[k] = W;
       s_T[k] = T;
       s_Z[k] = Z;
       s_bin[k] = chosen;
       s_above[k] = mb;
-      s_above_cnt[k] = cb;
-      s_cn[k] = (mode == MODE_LDS) ? (int)cnt[k][chosen] : 0;
+      // upper bound on the elements of the crossing bin: each carries at least the mass
+      // of x = (b+1)/16 (masses do not increase with x)
+      int ub = 0;
+      if (mode == MODE_LDS) {
+        const u64 qmin = fixed_mass(-((float)(chosen + 1) / kBinsPerNat));
+        const u64 mass = ms[k][chosen];
+        ub = qmin ? (int)min(mass / qmin + 1, (u64)kCandCap + 1) : kCandCap + 1;
+      }
+      s_fill[k] = ub;  // temporarily: the bound
     }
   }
   __syncthreads();
   if (tid == 0) {
     int off = 0;
     for (int k = 0; k < kDists; ++k) {
+      const int ub = s_fill[k];
       s_fill[k] = 0;
+      s_off[k] = 0;
+      s_ub[k] = ub;
       if (s_mode[k] != MODE_LDS) continue;
-      if (off + s_cn[k] <= kCandCap) {
+      if (off + ub <= kCandCap) {
         s_off[k] = off;
-        off += s_cn[k];
+        off += ub;
       } else {
         s_mode[k] = MODE_GLOBAL;
       }
@@ -350,14 +444,18 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
   }
   __syncthreads();
 
-  // ---- read 2: crossing-bin elements and keep-set candidates
-  int mode[kDists], binstar[kDists];
+  // ---- read 2: counts above the crossing bins, crossing-bin elements, keep-set candidates
+  int mode[kDists], binstar[kDists], boff[kDists], bub[kDists];
   float iz[kDists];
+  uint32_t above[kDists];
 #pragma unroll
   for (int k = 0; k < kDists; ++k) {
     mode[k] = s_mode[k];
     binstar[k] = s_bin[k];
+    boff[k] = s_off[k];
+    bub[k] = s_ub[k];
     iz[k] = s_iz[k];
+    above[k] = 0;
   }
   for (int base = 0; base < n; base += 256) {
     const int i = base + tid;
@@ -370,9 +468,11 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
       for (int k = 0; k < kDists; ++k) {
         const float v = v8[k];
         const float xv = M[k] - v;
-        if (mode[k] == MODE_LDS && x_bin(xv) == binstar[k]) {
+        const int bin = x_bin(xv);
+        above[k] += bin < binstar[k] ? 1u : 0u;
+        if (mode[k] == MODE_LDS && bin == binstar[k]) {
           const int p = atomicAdd(&s_fill[k], 1);
-          cand[s_off[k] + p] = v;
+          if (p < bub[k]) cand[boff[k] + p] = v;  // a count beyond the bound sends the row to the block path
         }
         imp = fmaxf(imp, exp2f(-xv * kLog2e) * iz[k]);
       }
@@ -393,6 +493,12 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
       __syncthreads();
     }
   }
+#pragma unroll
+  for (int k = 0; k < kDists; ++k) {
+    const uint32_t c = (uint32_t)wave_sum_int((int)above[k]);
+    if (lane == 0) atomicAdd(&s_above_cnt[k], c);
+  }
+  if (tid < kDists && s_mode[tid] == MODE_LDS && s_fill[tid] > s_ub[tid]) s_mode[tid] = MODE_GLOBAL;
   if (E > 0) {
     for (int j = s_kcount + tid; j < kKeepCap; j += 256) kbuf[j] = ~0ull;
     __syncthreads();
@@ -410,26 +516,33 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
   }
   __syncthreads();
 
-  // ---- exact refinement (wave w: rows 2w, 2w+1); the histogram space is free now
+  // ---- refinement: rows held in LDS by their wave, the others by the block
+  uint32_t* hcnt = reinterpret_cast<uint32_t*>(&ms[0][0]) + wave * 256;  // 4 x 1 KB (rows 0-1)
+  u64* hms = &ms[2][0] + wave * 256;                                      // 4 x 2 KB (rows 2-5)
   for (int d2 = 0; d2 < 2; ++d2) {
     const int k = 2 * wave + d2;
-    const int md = s_mode[k];
-    const bool act = md != MODE_DONE;
-    const bool glob = md == MODE_GLOBAL;
-    const float* src = glob ? x + k : cand + (act ? s_off[k] : 0);
-    const int m = glob ? n : (act ? s_cn[k] : 0);
-    const int Wr = wave_radix_refine(act, src, glob ? kDists : 1, m, M[k], s_T[k], glob ? 0ull : s_above[k],
-                                     glob ? 0u : s_above_cnt[k], &cnt[2 * wave][0], &ms[2 * wave][0],
-                                     lane, n);
-    if (lane == 0) {
-      const int W = act ? Wr : s_W[k];
-      a.ws_out[widx(k)] = W;
-      const float Zf = (float)((double)s_Z[k] / (double)kMassScale);
-      a.sp.stats[widx(k) * 2 + 1] = Zf;
-      if (a.stats_out) {
-        a.stats_out[widx(k) * 2] = M[k];
-        a.stats_out[widx(k) * 2 + 1] = Zf;
-      }
+    if (s_mode[k] == MODE_LDS) {
+      const int Wr = wave_refine_lds(cand + s_off[k], s_fill[k], M[k], s_T[k], s_above[k], s_above_cnt[k],
+                                     hcnt, hms, lane, n);
+      if (lane == 0) s_W[k] = Wr;
+    }
+  }
+  __syncthreads();
+  for (int k = 0; k < kDists; ++k) {
+    if (s_mode[k] != MODE_GLOBAL) continue;  // block-uniform
+    const int Wr = block_refine_global(x + k, n, s_bin[k], M[k], s_T[k], s_above[k], s_above_cnt[k],
+                                       reinterpret_cast<uint32_t*>(&ms[0][0]), &ms[2][0], s_red, tid);
+    if (tid == 0) s_W[k] = Wr;
+    __syncthreads();
+  }
+  if (tid < kDists) {
+    const int k = tid;
+    a.ws_out[widx(k)] = s_W[k];
+    const float Zf = (float)((double)s_Z[k] / (double)kMassScale);
+    a.sp.stats[widx(k) * 2 + 1] = Zf;
+    if (a.stats_out) {
+      a.stats_out[widx(k) * 2] = M[k];
+      a.stats_out[widx(k) * 2 + 1] = Zf;
     }
   }
 }
