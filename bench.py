@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=3000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=2.0e6,
+    ap.add_argument("--cpu-budget", type=float, default=5.0e6,
                     help="layer-tokens of oracle work in the CPU baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 4 GiB device copy (HBM counter calibration)")
