@@ -51,6 +51,10 @@ def parse():
                     help="layer-tokens of oracle work in the CPU baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 4 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--workload", choices=("boundary_sweep", "decode_loop"), default="boundary_sweep",
+                    help="boundary_sweep (default, the headline line) or decode_loop (the 36-layer "
+                         "decode loop: 128 requests x 4096 steps, reported on its own line)")
+    ap.add_argument("--decode-steps", type=int, default=4096)
     return ap.parse_args()
 
 
@@ -78,6 +82,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.workload == "decode_loop":
+        decode_loop(args)
         return
     import numpy as np
     import torch
@@ -190,6 +197,109 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(gw, backup, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def decode_loop(args):
+    """The decode loop on the Qwen3-8B shape: 128 requests from 1024-token prompts, 36
+    layers, every step updates both summaries and appends one K/V row per request, every
+    16th step all 128 requests run a boundary batch.  Input generation is outside the
+    timed region; every library call of every step is inside it (HIP events per step)."""
+    import numpy as np
+    import torch
+
+    from demand_paged_kv_amd import binding as Bd
+    from demand_paged_kv_amd.engine import BoundaryEngine
+    from synth.decode_loop import DecodeLoopGen, DecodeSpec
+
+    Bd.load()
+    spec = DecodeSpec(steps=args.decode_steps)
+    gen = DecodeLoopGen(spec, "cuda")
+    st = gen.initial_state()
+    torch.cuda.synchronize()
+    eng = BoundaryEngine(st, spec.B, spec.B * (spec.prompt + spec.steps + spec.P), Bd.params_from(spec.params))
+    req = torch.arange(spec.B, dtype=torch.int32, device="cuda")
+    acc = torch.zeros(Bd.GP_NUM_COUNTERS, dtype=torch.int64, device="cuda")
+    grows = torch.zeros(spec.B, dtype=torch.int64, device="cuda")
+    starts, ends, is_boundary = [], [], []
+    fill = 0
+    scanned = torch.zeros((), dtype=torch.int64, device="cuda")   # candidate slots of every scan
+    wall0 = time.time()
+    for t in range(spec.steps):
+        q, k, v = gen.step()
+        st.pos.fill_(spec.prompt + t)
+        fill += 1
+        boundary = fill == spec.P
+        if boundary:   # every write page fills on this step: n = (A + 1) * P per request
+            scanned += (st.n_alloc[: spec.B].to(torch.int64).sum() + spec.B) * spec.P
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        out = eng.decode_step(q, k, v, req, req if boundary else None)
+        e1.record()
+        starts.append(e0)
+        ends.append(e1)
+        is_boundary.append(boundary)
+        if boundary:
+            fill = 0
+            acc += eng.out.counters.to(torch.int64)
+            grows += out.decision[: spec.B].to(torch.int64)
+        if (t + 1) % 512 == 0:
+            torch.cuda.synchronize()
+            log(f"decode step {t + 1}/{spec.steps}: {time.time() - wall0:.1f}s wall")
+    torch.cuda.synchronize()
+    wall = time.time() - wall0
+    ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    ms_b = sum(m for m, bd in zip(ms, is_boundary) if bd)
+    ms_all = sum(ms)
+    c = dict(zip(Bd.COUNTER_NAMES, [int(x) for x in acc.cpu().numpy()]))
+    assert c["grow_denied"] == 0 and c["deferred"] == 0, c
+    # pool invariant after the run: every page's refcount equals its page-table references
+    n_alloc = st.n_alloc[: spec.B].to(torch.int64)
+    cols = torch.arange(spec.max_pages, device="cuda")[None, :]
+    ref = st.page_table[: spec.B][cols <= n_alloc[:, None]].to(torch.int64)
+    refs = torch.bincount(ref, minlength=spec.num_pages)
+    assert torch.equal(refs.to(torch.int32), st.refcount), "refcounts do not match the page tables"
+    assert int(st.free_top.item()) + int((refs > 0).sum().item()) == spec.num_pages
+    L, Hq, Hkv, d = spec.L, spec.Hq, spec.Hkv, spec.d
+    n_bound = int(sum(is_boundary))
+    ema_bytes = spec.steps * spec.B * L * Hq * d * (2 + 16)
+    append_bytes = spec.steps * spec.B * L * Hkv * d * 2 * 2 * 2
+    scanned = int(scanned.item())
+    scan_bytes = L * Hkv * scanned * d * 2 + n_bound * 2 * spec.B * L * Hq * d * 4
+    move_bytes = c["moved_rows"] * 4 * d * 2
+    alg = ema_bytes + append_bytes + scan_bytes + move_bytes
+    s_all = ms_all / 1e3
+    result = {
+        "metric": METRIC,
+        "value": round(n_bound * spec.B / s_all, 2),
+        "unit": "scans/s",
+        "n_gpus": 1,
+        "steps": spec.steps,
+        "warmup": 0,
+        "ms_per_step": round(ms_all / spec.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"decode_loop: 128 requests x 36 layers, 32q/8kv heads, d128, bf16 K/V, page 16, "
+                               f"1024-token prompts, {spec.steps} decode steps, boundary every 16 steps",
+                   "requests": spec.B, "layers": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "page_size": spec.P, "prompt": spec.prompt, "pool_pages": spec.num_pages,
+                   "top_p": spec.params["top_p"], "n_local": spec.params["n_local"], "seed": spec.seed},
+        "boundary_batches": n_bound,
+        "scans": n_bound * spec.B,
+        "tokens_scanned_per_s": round(L * scanned / s_all, 1),
+        "algorithmic_GBps": round(alg / s_all / 1e9, 1),
+        "hbm_frac": round(alg / s_all / 1e9 / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes": {"ema": ema_bytes, "append": append_bytes, "scan": scan_bytes,
+                              "compact_move": move_bytes},
+        "engine_ms": {"all_steps": round(ms_all, 2), "boundary_steps": round(ms_b, 2),
+                      "other_steps": round(ms_all - ms_b, 2)},
+        "wall_s_including_generation": round(wall, 2),
+        "grows": int(grows.sum().item()),
+        "counters": c,
+    }
     print(json.dumps(result), flush=True)
 
 

@@ -130,3 +130,22 @@ class BoundaryEngine:
         B.update_summaries(q, qd, (q.stride(0), q.stride(1), q.stride(2)), req_ids,
                            int(req_ids.numel()), st.L, st.Hq, st.d, st.sum_s, st.sum_l, self.prm,
                            stream)
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor, req_ids: torch.Tensor,
+               status_out: Optional[torch.Tensor] = None, stream=None):
+        """k_new, v_new: [n][L][Hkv][d] of the pool dtype, contiguous."""
+        assert k_new.is_contiguous() and v_new.is_contiguous()
+        B.append_kv(self.kv, self.pages, k_new, v_new, req_ids, int(req_ids.numel()), status_out,
+                    stream)
+
+    def decode_step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                    req_ids: torch.Tensor, boundary_ids: Optional[torch.Tensor] = None,
+                    stream=None) -> Optional[StepOutputs]:
+        """One decode step: summaries absorb q, the step's K/V row is appended, then the
+        entries in ``boundary_ids`` (those whose write page just filled) run one boundary
+        batch.  The caller keeps ``st.pos`` at the step's absolute position."""
+        self.update_summaries(q, req_ids, stream)
+        self.append(k_new, v_new, req_ids, None, stream)
+        if boundary_ids is None or boundary_ids.numel() == 0:
+            return None
+        return self.step(boundary_ids, stream)

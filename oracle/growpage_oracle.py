@@ -415,3 +415,91 @@ def boundary_step(wl, sum_s: np.ndarray, sum_l: np.ndarray, params: dict) -> Ste
     counters["freed_pages"] = len(freed)
     return StepResult(W, Wlo, Whi, M, Z, delta, dlo, dhi, raw, decision, amb, status, evicted, near,
                       imps, e_req, table, A, fill, refcount, stack, top, k_new, v_new, cow, counters)
+
+
+# ----------------------------------------------------------------------------- decode loop
+@dataclasses.dataclass
+class LoopState:
+    """Requests between decode steps as the oracle tracks them: stored rows in logical
+    slot order ([L][Hkv][n][d] per request), the page state and the summaries.  ``pos``
+    is the absolute position of the current step's query and token."""
+    L: int
+    Hq: int
+    Hkv: int
+    d: int
+    P: int
+    dtype: str
+    num_pages: int
+    page_table: np.ndarray
+    n_alloc: np.ndarray
+    fill: np.ndarray
+    refcount: np.ndarray
+    free_stack: np.ndarray
+    free_top: int
+    k_rows: list
+    v_rows: list
+    sum_s: np.ndarray
+    sum_l: np.ndarray
+    pos: np.ndarray
+    rope_cos: Optional[np.ndarray]
+    rope_sin: Optional[np.ndarray]
+
+    @property
+    def B(self) -> int:
+        return int(self.page_table.shape[0])
+
+    def n(self, b: int) -> int:
+        return int(self.n_alloc[b]) * self.P + int(self.fill[b])
+
+    def subset(self, idx) -> "LoopState":
+        """The requests ``idx`` (in that order) over the shared pool state."""
+        idx = np.asarray(idx, np.int64)
+        return LoopState(self.L, self.Hq, self.Hkv, self.d, self.P, self.dtype, self.num_pages,
+                         self.page_table[idx].copy(), self.n_alloc[idx].copy(), self.fill[idx].copy(),
+                         self.refcount.copy(), self.free_stack.copy(), int(self.free_top),
+                         [self.k_rows[b] for b in idx], [self.v_rows[b] for b in idx],
+                         self.sum_s[idx], self.sum_l[idx], self.pos[idx].copy(),
+                         self.rope_cos, self.rope_sin)
+
+
+def append_token(state: LoopState, b: int, k_new: np.ndarray, v_new: np.ndarray) -> bool:
+    """The step's K/V row [L][Hkv][d] of request b goes to slot A*P + fill, i.e. the next
+    slot of the write page (reading R6); a full write page takes nothing (False)."""
+    if int(state.fill[b]) >= state.P:
+        return False
+    state.k_rows[b] = np.concatenate([state.k_rows[b], np.asarray(k_new)[:, :, None, :]], axis=2)
+    state.v_rows[b] = np.concatenate([state.v_rows[b], np.asarray(v_new)[:, :, None, :]], axis=2)
+    state.fill[b] += 1
+    return True
+
+
+def decode_step(state: LoopState, q: np.ndarray, q_dtype: str, k_new: np.ndarray,
+                v_new: np.ndarray, params: dict):
+    """One decode step of every request, in place.
+
+    The summaries absorb the step's query first (R3; [Summary]: the summaries smooth the
+    decode queries), the step's row is appended (R6), and the requests whose write page
+    is now full form one boundary batch in batch order (boundary_step).  Positions then
+    advance by one.  Returns (appended [B] bool, boundary request indices, the boundary
+    batch's input state, StepResult); the last two are None when no write page filled."""
+    qf = query_f32(q, q_dtype)
+    state.sum_s = ema_update(state.sum_s, qf, params["beta_s"])
+    state.sum_l = ema_update(state.sum_l, qf, params["beta_l"])
+    appended = np.array([append_token(state, b, k_new[b], v_new[b]) for b in range(state.B)])
+    idx = np.flatnonzero(state.fill == state.P)
+    sub = res = None
+    if idx.size:
+        sub = state.subset(idx)
+        res = boundary_step(sub, sub.sum_s, sub.sum_l, params)
+        state.page_table[idx] = res.page_table
+        state.n_alloc[idx] = res.n_alloc
+        state.fill[idx] = res.fill
+        state.refcount = res.refcount.copy()
+        state.free_stack = res.free_stack.copy()
+        state.free_top = int(res.free_top)
+        for i, b in enumerate(idx):
+            if i in res.k_new:
+                state.k_rows[b] = res.k_new[i]
+                state.v_rows[b] = res.v_new[i]
+    state.pos = state.pos + 1
+    return appended, idx, sub, res

@@ -30,6 +30,7 @@ class Report:
     ev_near: int = 0
     ev_near_differs: int = 0
     decisions_ambiguous: int = 0
+    diverged: list = dataclasses.field(default_factory=list)   # requests whose keep-set took the other side of a near-tie
 
 
 def snapshot(st):
@@ -187,6 +188,10 @@ def compare_requests(wl, batch_idx, st, out, res: O.StepResult, n_local: int) ->
                     if res.evict_near_tie[i][l, g]:
                         rep.ev_near += 1
                         assert O.keep_set_valid(e, res.imp[i][l, g], k, n_local)
+                        if not np.array_equal(e, res.evicted[i][l, g]):
+                            rep.ev_near_differs += 1
+                            if i not in rep.diverged:
+                                rep.diverged.append(i)
                     else:
                         assert np.array_equal(e, res.evicted[i][l, g]), (i, l, g)
                     kept = np.setdiff1d(np.arange(wl.n(i)), e)

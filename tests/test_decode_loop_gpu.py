@@ -1,0 +1,143 @@
+"""Decode-loop parity on the Qwen3-8B shape (36 layers, 32 query / 8 KV heads, d 128, bf16,
+page 16, 1024-token prompts): every decode step updates both summaries and appends one
+K/V row per request; every 16 steps all write pages fill and the batch runs a boundary.
+
+* end to end at reduced size (4 requests x 4 layers x 512 steps): the oracle runs the
+  whole loop on its own from the same generated inputs; summaries are compared bit for
+  bit after every step and each of the 32 boundary batches element by element (working
+  sets, statistics, decisions, keep-sets, page table, refcounts, free stack, page bytes);
+* at the full batch shape (128 requests x 36 layers, 256 steps): three sampled requests are
+  tracked by the oracle from their own inputs; the whole batch is checked by pool
+  invariants at every boundary.
+
+A keep-set near-tie that the GPU resolves the other way (allowed, and validated) makes
+the two trajectories differ from then on; the request's comparison stops there and the
+test says so.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from tests import decode_util as DU
+from tests.parity_util import check_pool, compare_requests, compare_step, snapshot
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _engine(spec, st):
+    from demand_paged_kv_amd import binding as Bd
+    from demand_paged_kv_amd.engine import BoundaryEngine
+    max_tokens = spec.B * (spec.prompt + spec.steps + spec.P)
+    return BoundaryEngine(st, spec.B, max_tokens, Bd.params_from(spec.params))
+
+
+def _gpu_step(eng, st, spec, t, q, k, v, fill, req):
+    """One GPU decode step; ``fill`` is the host's count of rows in each write page."""
+    st.pos.fill_(spec.prompt + t)
+    fill += 1
+    bids = np.flatnonzero(fill == spec.P).astype(np.int32)
+    bt = torch.as_tensor(bids, device="cuda") if bids.size else None
+    out = eng.decode_step(q, k, v, req, bt)
+    torch.cuda.synchronize()
+    if out is not None:
+        deferred = (out.status[: bids.size].cpu().numpy() & 2) != 0
+        fill[bids[~deferred]] = 0
+    return bids, out
+
+
+def test_decode_loop_end_to_end_reduced():
+    from synth.decode_loop import DecodeLoopGen, DecodeSpec
+    spec = DecodeSpec(B=4, L=4, steps=512, seed=4000)
+    gen = DecodeLoopGen(spec, "cuda")
+    st = gen.initial_state()
+    ost = DU.oracle_state(st, np.arange(spec.B))
+    eng = _engine(spec, st)
+    req = torch.arange(spec.B, dtype=torch.int32, device="cuda")
+    fill = np.zeros(spec.B, np.int64)
+    n_local = spec.params["n_local"]
+    boundaries = compared = 0
+    decisions = []
+    diverged_at = None
+    for t in range(spec.steps):
+        q, k, v = gen.step()
+        bids, out = _gpu_step(eng, st, spec, t, q, k, v, fill, req)
+        app, idx, sub, res = O.decode_step(ost, DU.bits(q), "bf16", DU.bits(k), DU.bits(v), spec.params)
+        assert app.all()
+        assert np.array_equal(st.sum_s.cpu().numpy().view(np.uint32), ost.sum_s.view(np.uint32)), t
+        assert np.array_equal(st.sum_l.cpu().numpy().view(np.uint32), ost.sum_l.view(np.uint32)), t
+        assert np.array_equal(idx, bids), (t, idx, bids)
+        if res is None:
+            continue
+        boundaries += 1
+        if diverged_at is None:
+            rep = compare_step(sub, idx, st, out, res, n_local)
+            compared += 1
+            decisions.append(res.decision.copy())
+            if rep.ev_near_differs:
+                diverged_at = t
+                _say(f"[decode] step {t}: a keep-set near-tie resolved the other way; "
+                     f"page comparison stops here")
+        if boundaries % 8 == 0:
+            _say(f"[decode] step {t}: {boundaries} boundaries, {compared} compared")
+    dec = np.concatenate(decisions)
+    _say(f"[decode] {boundaries} boundaries, {compared} compared, grows {int(dec.sum())} of {dec.size}")
+    assert boundaries == spec.steps // spec.P
+    assert compared >= boundaries // 2
+    assert 0 < dec.sum() < dec.size, "both decisions should occur"
+
+
+def test_decode_loop_full_shape_sampled():
+    from synth.decode_loop import DecodeLoopGen, DecodeSpec
+    spec = DecodeSpec(B=128, L=36, steps=256, seed=4001)
+    gen = DecodeLoopGen(spec, "cuda")
+    st = gen.initial_state()
+    track = np.array([5, 77, 126])
+    ost = DU.oracle_state(st, track)
+    eng = _engine(spec, st)
+    req = torch.arange(spec.B, dtype=torch.int32, device="cuda")
+    fill = np.zeros(spec.B, np.int64)
+    n_local = spec.params["n_local"]
+    live = np.ones(track.size, bool)
+    boundaries = 0
+    grows = 0
+    _say(f"[decode-full] generated {spec.B} requests x {spec.L} layers; tracking {track.tolist()}")
+    for t in range(spec.steps):
+        q, k, v = gen.step()
+        before = snapshot(st) if fill[0] + 1 == spec.P else None
+        bids, out = _gpu_step(eng, st, spec, t, q, k, v, fill, req)
+        app, idx, sub, res = O.decode_step(ost, DU.bits(q[track]), "bf16", DU.bits(k[track]),
+                                           DU.bits(v[track]), spec.params)
+        assert app.all()
+        s_gpu = st.sum_s[torch.as_tensor(track, device="cuda")].cpu().numpy()
+        l_gpu = st.sum_l[torch.as_tensor(track, device="cuda")].cpu().numpy()
+        assert np.array_equal(s_gpu.view(np.uint32), ost.sum_s.view(np.uint32)), t
+        assert np.array_equal(l_gpu.view(np.uint32), ost.sum_l.view(np.uint32)), t
+        if out is None:
+            assert res is None
+            continue
+        assert bids.size == spec.B and idx.size == track.size
+        boundaries += 1
+        dec = out.decision[: spec.B].cpu().numpy()
+        grows += int(dec.sum())
+        assert not out.status[: spec.B].cpu().numpy().any()
+        check_pool(st, before, dec, np.arange(spec.B))
+        keep = np.flatnonzero(live)
+        if keep.size == track.size:
+            rep = compare_requests(sub, track, st, out, res, n_local)
+        elif keep.size:
+            sub_live = sub.subset(keep)
+            res_live = O.boundary_step(sub_live, sub_live.sum_s, sub_live.sum_l, spec.params)
+            rep = compare_requests(sub_live, track[keep], st, out, res_live, n_local)
+        for i in rep.diverged if keep.size else []:
+            _say(f"[decode-full] step {t}: request {track[keep[i]]} took the other side of a "
+                 f"keep-set near-tie; its comparison ends here")
+            live[keep[i]] = False
+        _say(f"[decode-full] step {t}: boundary {boundaries}, grows so far {grows}, "
+             f"tracked {int(live.sum())}")
+    assert boundaries == spec.steps // spec.P
+    assert live.sum() >= 2

@@ -376,3 +376,92 @@ def test_paper_hyperparameters_fixture():
     assert SW.PARAMS_PAPER["beta_s"] == g["beta_s"] and SW.PARAMS_PAPER["beta_l"] == g["beta_l"]
     assert SW.PARAMS_PAPER["top_p"] == g["top_p"] and SW.PARAMS_PAPER["tau"] == g["tau"]
     assert SW.PARAMS_PAPER["n_local"] == g["local_retention_quota"]
+
+
+# ----------------------------------------------------------------------------- decode loop
+def _tiny_loop(P=4, A=2, d=8, Hq=4, beta_s=0.9, top_p=0.9, n_local=0, seed=0):
+    """One request, one layer, one KV head, f32 rows; the write page starts empty."""
+    rng = np.random.default_rng(seed)
+    n = A * P
+    k = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+    v = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+    num_pages = 8
+    table = np.full((1, 6), -1, np.int64)
+    table[0, : A + 1] = np.arange(A + 1)
+    rc = np.zeros(num_pages, np.int64)
+    rc[: A + 1] = 1
+    stack = np.zeros(num_pages, np.int64)
+    stack[: num_pages - A - 1] = np.arange(A + 1, num_pages)
+    prm = dict(beta_s=beta_s, beta_l=0.999, top_p=top_p, tau=0, n_local=n_local)
+    st = O.LoopState(1, Hq, 1, d, P, "f32", num_pages, table, np.array([A]), np.array([0]), rc, stack,
+                     num_pages - A - 1, [k], [v], np.zeros((1, 1, Hq, d), np.float32),
+                     np.zeros((1, 1, Hq, d), np.float32), np.array([n]), None, None)
+    return st, prm
+
+
+def test_decode_boundary_fires_when_write_page_fills_and_scans_new_token():
+    """p = 1 makes W = n exactly (R1), so W tells how many slots the scan saw: the boundary
+    comes on the P-th append and its scan includes that step's row (R6)."""
+    P, A, d = 4, 2, 8
+    st, prm = _tiny_loop(P, A, d, top_p=1.0)
+    rng = np.random.default_rng(1)
+    for t in range(P):
+        q = rng.standard_normal((1, 1, 4, d)).astype(np.float32)
+        kn = rng.standard_normal((1, 1, 1, d)).astype(np.float32)[:, :, 0]
+        app, idx, sub, res = O.decode_step(st, q, "f32", kn[None], kn[None], prm)
+        assert app.all()
+        if t < P - 1:
+            assert res is None and st.fill[0] == t + 1
+    assert list(idx) == [0]
+    assert np.all(res.W == (A + 1) * P)
+    assert res.decision[0] == O.DECISION_COMPACT          # delta = 0 with W = n on both sides
+    assert st.fill[0] == 0 and st.k_rows[0].shape[2] == A * P
+    assert st.pos[0] == A * P + P                          # one position per step
+
+
+def test_decode_summaries_absorb_the_query_before_the_scan():
+    """With beta_S = 0 the short summary is the step's query (R3).  The last query points at
+    a key planted far out, so the short working set is 1 only if the boundary scan sees the
+    summary after this step's update."""
+    P, A, d = 4, 2, 8
+    st, prm = _tiny_loop(P, A, d, beta_s=0.0, top_p=0.5)
+    u = np.zeros(d, np.float32)
+    u[0] = 1.0
+    st.k_rows[0][0, 0, 3] = 40.0 * u                      # a key along u at slot 3
+    zero = np.zeros((1, 1, 1, d), np.float32)
+    for t in range(P):
+        q = np.zeros((1, 1, 4, d), np.float32)
+        if t == P - 1:
+            q[:] = 4.0 * u                                 # only the last query points at it
+        app, idx, sub, res = O.decode_step(st, q, "f32", zero[:, :, 0][None], zero[:, :, 0][None], prm)
+    assert res is not None
+    assert np.all(res.W[0, 0, :, 0] == 1)
+
+
+def test_decode_full_write_page_takes_nothing():
+    P, A, d = 4, 2, 8
+    st, prm = _tiny_loop(P, A, d)
+    st.fill[0] = P
+    st.k_rows[0] = np.concatenate([st.k_rows[0], np.zeros((1, 1, P, d), np.float32)], axis=2)
+    st.v_rows[0] = np.concatenate([st.v_rows[0], np.zeros((1, 1, P, d), np.float32)], axis=2)
+    before = st.k_rows[0].copy()
+    assert not O.append_token(st, 0, np.ones((1, 1, d), np.float32), np.ones((1, 1, d), np.float32))
+    assert st.fill[0] == P and np.array_equal(st.k_rows[0], before)
+
+
+def test_decode_compaction_keeps_a_stable_subset():
+    P, A, d = 4, 3, 8
+    st, prm = _tiny_loop(P, A, d, seed=3)
+    rng = np.random.default_rng(4)
+    rows_seen = None
+    for t in range(P):
+        q = rng.standard_normal((1, 1, 4, d)).astype(np.float32) * 3
+        kn = rng.standard_normal((1, 1, d)).astype(np.float32)
+        if t == P - 1:
+            rows_seen = np.concatenate([st.k_rows[0], kn[None, :, :, None, :][0]], axis=2).copy()
+        app, idx, sub, res = O.decode_step(st, q, "f32", kn[None], kn[None], prm)
+    assert res.decision[0] == O.DECISION_COMPACT or st.n_alloc[0] == A + 1
+    if res.decision[0] == O.DECISION_COMPACT:
+        kept = np.setdiff1d(np.arange((A + 1) * P), res.evicted[0][0, 0])
+        assert np.array_equal(st.k_rows[0][0, 0], rows_seen[0, 0][kept])
+        assert st.k_rows[0].shape[2] == A * P
