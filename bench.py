@@ -51,9 +51,12 @@ def parse():
                     help="layer-tokens of oracle work in the CPU baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 4 GiB device copy (HBM counter calibration)")
-    ap.add_argument("--workload", choices=("boundary_sweep", "decode_loop"), default="boundary_sweep",
-                    help="boundary_sweep (default, the headline line) or decode_loop (the 36-layer "
-                         "decode loop: 128 requests x 4096 steps, reported on its own line)")
+    ap.add_argument("--workload", choices=("boundary_sweep", "decode_loop", "prefix_share"),
+                    default="boundary_sweep",
+                    help="boundary_sweep (default, the headline line); decode_loop (the 36-layer decode "
+                         "loop: 128 requests x 4096 steps) or prefix_share (256 requests x 36 layers, page "
+                         "32, shared 2048-token prefixes, pool at 80%% of demand; one shot), each reported "
+                         "on its own line")
     ap.add_argument("--decode-steps", type=int, default=4096)
     return ap.parse_args()
 
@@ -85,6 +88,9 @@ def main():
         return
     if args.workload == "decode_loop":
         decode_loop(args)
+        return
+    if args.workload == "prefix_share":
+        prefix_share(args)
         return
     import numpy as np
     import torch
@@ -298,6 +304,67 @@ def decode_loop(args):
                       "other_steps": round(ms_all - ms_b, 2)},
         "wall_s_including_generation": round(wall, 2),
         "grows": int(grows.sum().item()),
+        "counters": c,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def prefix_share(args):
+    """One boundary batch of the prefix-sharing stress (no room for a state backup, so a
+    single timed step): 256 requests x 36 layers, page 32, groups of 16 sharing a 64-page
+    prefix, contexts log-uniform in [1024, 32768], pool at 80% of the full-KV demand."""
+    import numpy as np
+    import torch
+
+    from demand_paged_kv_amd import binding as Bd
+    from demand_paged_kv_amd.engine import BoundaryEngine
+    from synth import gpu_workloads as GW
+
+    Bd.load()
+    t0 = time.time()
+    gw = GW.prefix_share(seed=5000)
+    st = gw.st
+    torch.cuda.synchronize()
+    log(f"workload generated in {time.time() - t0:.1f}s: {gw.B} requests, {gw.total_tokens()} tokens, "
+        f"pool {st.num_pages} pages, free {int(st.free_top.item())}")
+    eng = BoundaryEngine(st, gw.B, gw.total_tokens(), Bd.params_from(gw.params))
+    req = torch.arange(gw.B, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    names = ("scan", "decide", "compact_prepare", "compact_move")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    ev[0].record()
+    eng.scan(req)
+    ev[1].record()
+    eng.decide(req)
+    ev[2].record()
+    eng.compact_prepare(req)
+    ev[3].record()
+    eng.compact_move(req)
+    ev[4].record()
+    torch.cuda.synchronize()
+    c = dict(zip(Bd.COUNTER_NAMES, [int(x) for x in eng.out.counters.cpu().numpy()]))
+    ms = ev[0].elapsed_time(ev[4])
+    L, Hq, Hkv, d = st.L, st.Hq, st.Hkv, st.d
+    sum_n = gw.total_tokens()
+    scan_bytes = L * Hkv * sum_n * d * 2 + 2 * gw.B * L * Hq * d * 4
+    move_bytes = c["moved_rows"] * 4 * d * 2
+    cow_bytes = c["copied_rows"] * 2 * 2 * d * 2
+    alg = scan_bytes + move_bytes + cow_bytes
+    s_ = ms / 1e3
+    result = {
+        "metric": METRIC, "value": round(gw.B / s_, 2), "unit": "scans/s", "n_gpus": 1, "steps": 1,
+        "warmup": 0, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "prefix_share: 256 requests x 36 layers, 32q/8kv heads, d128, bf16 K/V, page 32, "
+                               "groups of 16 sharing a 2048-token prefix, contexts log-uniform 1024-32768, "
+                               "pool 80% of full-KV demand",
+                   "requests": gw.B, "layers": L, "page_size": st.P, "tokens": sum_n,
+                   "pool_pages": st.num_pages, "seed": gw.seed},
+        "tokens_scanned_per_s": round(L * sum_n / s_, 1),
+        "algorithmic_GBps": round(alg / s_ / 1e9, 1),
+        "hbm_frac": round(alg / s_ / 1e9 / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes": {"scan": scan_bytes, "compact_move": move_bytes, "copy_on_write": cow_bytes},
+        "breakdown_ms": {k: round(ev[i].elapsed_time(ev[i + 1]), 4) for i, k in enumerate(names)},
         "counters": c,
     }
     print(json.dumps(result), flush=True)

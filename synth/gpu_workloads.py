@@ -119,6 +119,110 @@ def boundary_sweep(seed: int = 3000, B: int = 64, L: int = 32, Hq: int = 32, Hkv
     return GpuWorkload(st, n, A, regime, pos, dict(params or SW.PARAMS_DEFAULT), seed, name)
 
 
+def prefix_share(seed: int = 5000, B: int = 256, L: int = 36, Hq: int = 32, Hkv: int = 8, d: int = 128,
+                 P: int = 32, ctx=(1024, 32768), group: int = 16, prefix_pages: int = 64,
+                 pool_frac: float = 0.8, alloc_frac: float = 0.8, grow_frac: float = 0.3, s_range=(0.8, 1.6),
+                 free_pages: int | None = None, params: dict | None = None, device="cuda",
+                 name: str = "prefix_share") -> GpuWorkload:
+    """Prefix-sharing stress: groups of ``group`` consecutive requests share their first
+    ``prefix_pages`` pages (refcount = group), contexts log-uniform in ``ctx``, Zipf
+    exponent per request uniform in ``s_range``.  The pool holds ``pool_frac`` of the
+    full-KV demand (every request's ceil(c/P) pages, a shared prefix counted once); each
+    request's allocation is scaled to A = max(prefix_pages, floor(alloc_frac * c / P)), so
+    the free stack starts nearly empty and compactions that reach into a shared prefix
+    need copy-on-write pages the stack may not have (``free_pages`` instead sets the
+    stack's size directly).  Every request is at its boundary.
+    Members of a group share their summary directions (same prompt); prefix keys carry
+    the Zipf profile of the group's first request."""
+    rng = np.random.default_rng(seed)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    G = Hq // Hkv
+    c = np.exp(rng.uniform(math.log(ctx[0]), math.log(ctx[1]), size=B))
+    n_groups = (B + group - 1) // group
+    sizes = np.array([min(group, B - g * group) for g in range(n_groups)])
+    demand = int(np.ceil(c / P).sum()) - int(((sizes - 1) * prefix_pages).sum())
+    num_pages = int(pool_frac * demand)
+    A = np.maximum(prefix_pages, np.floor(alloc_frac * c / P)).astype(np.int64)
+    n = (A + 1) * P
+    used = int((A + 1).sum()) - int(((sizes - 1) * prefix_pages).sum())
+    if free_pages is not None:
+        num_pages = used + int(free_pages)
+    assert used <= num_pages, "pool too small for the drawn contexts"
+    s_zipf = rng.uniform(s_range[0], s_range[1], size=B)
+    pos = (n + rng.integers(0, 64, size=B)).astype(np.int64)
+    regime = np.zeros(B, np.int32)
+    regime[rng.choice(B, size=int(round(grow_frac * B)), replace=False)] = 1
+    max_pages = int(A.max()) + 8
+    perm = rng.permutation(num_pages)
+    table = np.full((B, max_pages), -1, np.int32)
+    refcount = np.zeros(num_pages, np.int32)
+    cur = 0
+    for g in range(n_groups):
+        pre = perm[cur: cur + prefix_pages]
+        cur += prefix_pages
+        refcount[pre] = sizes[g]
+        for b in range(g * group, g * group + sizes[g]):
+            table[b, :prefix_pages] = pre
+            k = int(A[b]) + 1 - prefix_pages
+            table[b, prefix_pages: A[b] + 1] = perm[cur: cur + k]
+            refcount[perm[cur: cur + k]] = 1
+            cur += k
+    free = perm[cur:]
+    stack = np.zeros(num_pages, np.int32)
+    stack[: len(free)] = free
+
+    cos_np, sin_np = SW.rope_tables(int(pos.max()) + 1, d)
+    cos = torch.from_numpy(cos_np).to(device)
+    sin = torch.from_numpy(sin_np).to(device)
+    u = torch.randn((n_groups, L, Hq, d), generator=gen, device=device, dtype=torch.float64)
+    u = u / u.norm(dim=-1, keepdim=True)
+    ug = u[torch.from_numpy(np.arange(B) // group).to(device)]                       # [B][L][Hq][d]
+    reg = torch.from_numpy(regime).to(device).bool()[:, None, None]
+    U = lambda lo, hi: lo + (hi - lo) * torch.rand((B, L, Hq), generator=gen, device=device, dtype=torch.float64)
+    bs = torch.where(reg, U(0.2, 0.8), U(2.0, 5.0))
+    bl = torch.where(reg, U(1.5, 3.0), U(0.5, 1.5))
+    sum_s = (bs[..., None] * ug + 0.1 * torch.randn((B, L, Hq, d), generator=gen, device=device, dtype=torch.float64)).float()
+    sum_l = (bl[..., None] * ug + 0.1 * torch.randn((B, L, Hq, d), generator=gen, device=device, dtype=torch.float64)).float()
+
+    k_pool = torch.empty((L, num_pages, Hkv, P, d), dtype=torch.bfloat16, device=device)
+    v_pool = torch.empty_like(k_pool)
+    for l in range(L):
+        k_pool[l].normal_(generator=gen)
+        v_pool[l].normal_(generator=gen)
+    pre_len = prefix_pages * P
+
+    def plant(b, lo, hi):
+        """Keys of slots [lo, hi) of request b: N(0, I) plus b's Zipf profile."""
+        nb = int(n[b])
+        scale = float(s_zipf[b]) * math.sqrt(d) / 2.0
+        dirs = _rotate(ug[b], cos[pos[b]].double(), sin[pos[b]].double()).float()   # [L][Hq][d]
+        k = torch.randn((L, Hkv, hi - lo, d), generator=gen, device=device, dtype=torch.float32)
+        for j in range(G):
+            rank = torch.argsort(torch.rand((L, Hkv, nb), generator=gen, device=device), dim=-1)
+            rank = rank[..., lo:hi].float() + 1.0
+            mu = scale * (math.log(nb) - torch.log(rank))
+            k += mu[..., None] * dirs[:, j::G][:, :, None, :]
+        pages = torch.from_numpy(table[b, lo // P: hi // P].astype(np.int64)).to(device)
+        k_pool[:, pages] = k.to(torch.bfloat16).view(L, Hkv, (hi - lo) // P, P, d).permute(0, 2, 1, 3, 4)
+
+    for g in range(n_groups):
+        plant(g * group, 0, pre_len)
+    for b in range(B):
+        plant(b, pre_len, int(n[b]))
+    st = DeviceState(L=L, Hq=Hq, Hkv=Hkv, d=d, P=P, num_pages=num_pages, dtype=Bd.GP_BF16,
+                     k_pool=k_pool, v_pool=v_pool,
+                     page_table=torch.from_numpy(table).to(device),
+                     n_alloc=torch.from_numpy(A.astype(np.int32)).to(device),
+                     fill=torch.full((B,), P, dtype=torch.int32, device=device),
+                     refcount=torch.from_numpy(refcount).to(device),
+                     free_stack=torch.from_numpy(stack).to(device),
+                     free_top=torch.tensor([len(free)], dtype=torch.int32, device=device),
+                     sum_s=sum_s.contiguous(), sum_l=sum_l.contiguous(),
+                     pos=torch.from_numpy(pos.astype(np.int32)).to(device), rope_cos=cos, rope_sin=sin)
+    return GpuWorkload(st, n, A, regime, pos, dict(params or SW.PARAMS_DEFAULT), seed, name)
+
+
 class StateBackup:
     """Device copy of everything a boundary batch mutates, to replay the same batch."""
 

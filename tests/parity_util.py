@@ -241,3 +241,153 @@ def run_step_gpu(wl, sum_s=None, sum_l=None, slots=None, max_req=None, params=No
     out = eng.step(req)
     torch.cuda.synchronize()
     return st, out, eng
+
+
+def compare_sampled(wl, batch_idx, st, out, params: dict) -> Report:
+    """Per-request checks that hold whatever the rest of the batch did: the oracle scans each
+    sampled request on its own (working sets, statistics, delta, the raw grow/compact
+    choice, the keep-set of every (layer, KV head)), and the GPU's page contents must be
+    the untouched rows (grown or deferred requests) or the stable compaction by the keep-set
+    (compacted ones).  Pops, denials, deferrals and pushes depend on the whole batch and
+    are checked by ``check_pool_shared``.  ``wl`` holds the sampled requests' rows from
+    before the step; ``batch_idx[i]`` is their batch position (== request slot)."""
+    rep = Report()
+    p = float(np.float32(params["top_p"]))
+    tau, n_local = int(params["tau"]), int(params["n_local"])
+    ws = out.ws.cpu().numpy()
+    stats = out.stats.cpu().numpy()
+    delta = out.delta.cpu().numpy()
+    dec = out.decision.cpu().numpy()
+    status = out.status.cpu().numpy()
+    ev_gpu = out.evicted.cpu().numpy()
+    table = st.page_table.cpu().numpy()
+    for i, b in enumerate(batch_idx):
+        cr, sr = wl.rope_cos[wl.pos[i]], wl.rope_sin[wl.pos[i]]
+        W, Wlo, Whi, M, Z, probs = O.scan_request(wl.k_rows[i], wl.dtype, wl.sum_s[i], wl.sum_l[i], cr, sr, p,
+                                                  keep_logits=True)
+        near = Wlo != Whi
+        rep.ws_total += int(W.size)
+        rep.ws_near += int(near.sum())
+        assert not (~near & (ws[b] != W)).any(), ("W mismatch", b)
+        assert not (near & ((ws[b] < Wlo) | (ws[b] > Whi))).any(), ("W outside near-tie range", b)
+        errM = np.abs(stats[b][..., 0] - M) / np.maximum(1.0, np.abs(M))
+        errZ = np.abs(stats[b][..., 1] - Z) / Z
+        assert errM.max() <= LOGIT_TOL and errZ.max() <= Z_RTOL, (b, errM.max(), errZ.max())
+        d0, dlo, dhi = O.delta_range(W, Wlo, Whi)
+        assert dlo <= delta[b] <= dhi, (b, delta[b], dlo, dhi)
+        if not near.any():
+            assert delta[b] == d0
+        raw_grow = d0 > tau
+        if (dlo <= tau) != (dhi <= tau):
+            rep.decisions_ambiguous += 1
+        else:
+            assert (delta[b] > tau) == raw_grow, b
+        n = wl.n(i)
+        k = int(wl.n_alloc[i]) * wl.P
+        compacted = dec[b] == O.DECISION_COMPACT and not (status[b] & O.REQ_DEFERRED)
+        if dec[b] == O.DECISION_COMPACT:
+            E = n - k
+            for l in range(wl.L):
+                for g in range(wl.Hkv):
+                    rep.ev_units += 1
+                    imp = O.importance(probs[l, g])
+                    kept, evd, nr = O.keep_set(imp, k, n_local)
+                    e = ev_gpu[b, l, g, :E]
+                    assert np.all(ev_gpu[b, l, g, E:] == -1)
+                    if nr:
+                        rep.ev_near += 1
+                        assert O.keep_set_valid(e, imp, k, n_local), (b, l, g)
+                        if not np.array_equal(e, evd):
+                            rep.ev_near_differs += 1
+                    else:
+                        assert np.array_equal(e, evd), (b, l, g, e, evd)
+        if compacted:
+            gk, gv = SD.read_rows(st, table[b], k, wl.dtype)
+            for l in range(wl.L):
+                for g in range(wl.Hkv):
+                    kept = np.setdiff1d(np.arange(n), ev_gpu[b, l, g, : n - k])
+                    assert np.array_equal(gk[l, g], wl.k_rows[i][l, g][kept]), ("K", b, l, g)
+                    assert np.array_equal(gv[l, g], wl.v_rows[i][l, g][kept]), ("V", b, l, g)
+        else:
+            gk, gv = SD.read_rows(st, table[b], n, wl.dtype)
+            assert np.array_equal(gk, wl.k_rows[i]) and np.array_equal(gv, wl.v_rows[i]), ("untouched", b)
+    return rep
+
+
+def check_pool_shared(st, before: dict, out, n_req: int, P: int, tau: int):
+    """Whole-batch page-state invariants with shared pages, from the pages' allocation
+    rules as read here: grows pop the stack top in batch order (denied when it is empty or
+    the page-table row is full); then compacting requests, in batch order, take fresh
+    pages for the shared pages (refcount > 1 before the step) from the first page their
+    compaction changes on, or are deferred untouched when the stack is short; pages whose
+    refcount reaches 0 are pushed in ascending order.  Replayed from the GPU's own deltas
+    and evicted slots (a consistency check of the page logic; the scan and keep-sets are
+    checked against the oracle elsewhere)."""
+    delta = out.delta.cpu().numpy()[:n_req]
+    dec = out.decision.cpu().numpy()[:n_req]
+    status = out.status.cpu().numpy()[:n_req]
+    ev = out.evicted.cpu().numpy()[:n_req]
+    table = before["page_table"].copy()
+    A = before["n_alloc"].astype(np.int64).copy()
+    fill = before["fill"].astype(np.int64).copy()
+    rc0 = before["refcount"].astype(np.int64)
+    rc = rc0.copy()
+    stack = before["free_stack"].astype(np.int64).copy()
+    top = int(before["free_top"])
+    want_status = np.zeros(n_req, np.int64)
+    want_dec = np.zeros(n_req, np.int64)
+    for b in range(n_req):
+        if fill[b] != P:
+            want_status[b] |= O.REQ_NOT_AT_BOUNDARY
+            continue
+        if delta[b] > tau:
+            if top > 0 and A[b] + 2 <= table.shape[1]:
+                top -= 1
+                pg = stack[top]
+                table[b, A[b] + 1] = pg
+                rc[pg] = 1
+                A[b] += 1
+                fill[b] = 0
+                want_dec[b] = O.DECISION_GROW
+            else:
+                want_status[b] |= O.REQ_GROW_DENIED
+    freed = []
+    for b in range(n_req):
+        if fill[b] != P or want_dec[b] == O.DECISION_GROW:
+            continue
+        n = int(A[b]) * P + P
+        e = ev[b][..., : P]
+        e_r = int(e.min()) if e.size else n
+        need = [j for j in range(e_r // P, int(A[b])) if rc0[table[b, j]] > 1]
+        if len(need) > top:
+            want_status[b] |= O.REQ_DEFERRED
+            continue
+        for j in need:
+            top -= 1
+            old = table[b, j]
+            table[b, j] = stack[top]
+            rc[stack[top]] = 1
+            rc[old] -= 1
+            if rc[old] == 0:
+                freed.append(old)
+        fill[b] = 0
+    for pg in sorted(freed):
+        stack[top] = pg
+        top += 1
+    assert np.array_equal(dec, want_dec), "decisions"
+    assert np.array_equal(status, want_status), "status bits"
+    g_table = st.page_table.cpu().numpy()
+    assert np.array_equal(g_table[:n_req], table[:n_req]), "page table"
+    assert np.array_equal(st.n_alloc.cpu().numpy()[:n_req], A), "n_alloc"
+    assert np.array_equal(st.fill.cpu().numpy()[:n_req], fill), "fill"
+    g_rc = st.refcount.cpu().numpy()
+    assert np.array_equal(g_rc, rc), "refcounts"
+    assert int(st.free_top.item()) == top, "free_top"
+    assert np.array_equal(st.free_stack.cpu().numpy()[:top], stack[:top]), "free stack"
+    refs = np.zeros_like(g_rc)
+    for b in range(n_req):
+        for j in range(int(A[b]) + 1):
+            refs[g_table[b, j]] += 1
+    assert np.array_equal(refs, g_rc), "refcount != references"
+    return dict(grows=int((want_dec == 1).sum()), denied=int(((want_status & O.REQ_GROW_DENIED) != 0).sum()),
+                deferred=int(((want_status & O.REQ_DEFERRED) != 0).sum()), freed=len(freed))
