@@ -58,6 +58,9 @@ def parse():
                          "32, shared 2048-token prefixes, pool at 80%% of demand; one shot), each reported "
                          "on its own line")
     ap.add_argument("--decode-steps", type=int, default=4096)
+    ap.add_argument("--paper", action="store_true",
+                    help="boundary sweep at the pages' operating point (KV block 256, p 0.99, quota 64), "
+                         "reported on its own line")
     return ap.parse_args()
 
 
@@ -101,7 +104,12 @@ def main():
 
     Bd.load()  # the HIP library must be there; no fallback
     t0 = time.time()
-    gw = GW.boundary_sweep(seed=args.seed)
+    if args.paper:
+        from synth import workloads as SW
+        gw = GW.boundary_sweep(seed=args.seed + 100, P=256, num_pages=1536, params=dict(SW.PARAMS_PAPER),
+                               name="boundary_sweep_paper")
+    else:
+        gw = GW.boundary_sweep(seed=args.seed)
     st = gw.st
     torch.cuda.synchronize()
     log(f"workload generated in {time.time() - t0:.1f}s: {gw.B} requests, {gw.total_tokens()} tokens, "
@@ -165,7 +173,7 @@ def main():
     try:
         with open(TRAFFIC_FILE) as fh:
             tf = json.load(fh)
-        if tf.get("source_hash") == source_hash() and tf.get("kernel_key") == dom:
+        if tf.get("source_hash") == source_hash() and tf.get("kernel_key") == dom and not args.paper:
             traffic = tf.get("bytes_per_launch")
     except (OSError, ValueError):
         pass
@@ -185,12 +193,15 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "boundary_sweep: 64 requests x 32 layers, 32q/8kv heads, d128, bf16 K/V, "
-                               "page 16, contexts log-uniform 512-16384, 30% planted broadening, "
-                               "24576-page pool",
+        "config": {"workload": ("boundary_sweep: 64 requests x 32 layers, 32q/8kv heads, d128, bf16 K/V, "
+                                "page 16, contexts log-uniform 512-16384, 30% planted broadening, "
+                                "24576-page pool") if not args.paper else
+                               ("boundary_sweep_paper: 64 requests x 32 layers, 32q/8kv heads, d128, bf16 K/V, "
+                                "page 256, p 0.99, quota 64, contexts log-uniform 512-16384, 30% planted "
+                                "broadening, 1536-page pool"),
                    "requests": gw.B, "layers": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "page_size": P, "tokens": sum_n, "pool_pages": st.num_pages, "top_p": gw.params["top_p"],
-                   "n_local": gw.params["n_local"], "seed": args.seed, "storage_dtype": "bf16"},
+                   "n_local": gw.params["n_local"], "seed": gw.seed, "storage_dtype": "bf16"},
         "tokens_scanned_per_s": round(L * sum_n / step_s, 1),
         "algorithmic_GBps": round(alg_bytes / step_s / 1e9, 1),
         "hbm_frac": round(alg_bytes / step_s / 1e9 / HBM_PEAK_GBPS, 4),

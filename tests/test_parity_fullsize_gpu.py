@@ -38,3 +38,28 @@ def test_boundary_sweep_full_size_sampled():
     # planted regimes come out as planted
     assert np.array_equal(dec, gw.regime.astype(np.uint8)), (dec, gw.regime)
     print("[fullsize]", rep, flush=True)
+
+
+def test_paper_operating_point_full_size_sampled():
+    """The sweep's shape at the pages' operating point: KV block 256, p 0.99, quota 64."""
+    from demand_paged_kv_amd import binding as Bd
+    from demand_paged_kv_amd.engine import BoundaryEngine
+    from synth import gpu_workloads as GW
+    from synth import workloads as SW
+
+    gw = GW.boundary_sweep(seed=3100, P=256, num_pages=1536, params=dict(SW.PARAMS_PAPER), name="paper_sweep")
+    st = gw.st
+    print(f"[paper] generated {gw.B} requests, {gw.total_tokens()} tokens", flush=True)
+    order = np.argsort(-gw.n)
+    sample = sorted({int(order[0]), int(order[-1]), int(np.flatnonzero(gw.regime == 1)[0]),
+                     int(np.flatnonzero(gw.regime == 0)[0])})
+    wl = GW.to_host_workload(gw, sample)
+    before = snapshot(st)
+    eng = BoundaryEngine(st, gw.B, gw.total_tokens(), Bd.params_from(gw.params))
+    out = eng.step(torch.arange(gw.B, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, gw.params)
+    rep = compare_requests(wl, sample, st, out, res, gw.params["n_local"])
+    dec = out.decision.cpu().numpy()
+    check_pool(st, before, dec, np.arange(gw.B))
+    print("[paper]", rep, "grows", int(dec.sum()), flush=True)

@@ -117,6 +117,12 @@ CASES = [
     ("p_one", dict(B=3, L=1, Hq=8, Hkv=2, d=64, P=16, params=dict(SW.PARAMS_DEFAULT, top_p=1.0))),
     ("p_zero", dict(B=3, L=1, Hq=8, Hkv=2, d=64, P=16, params=dict(SW.PARAMS_DEFAULT, top_p=0.0))),
     ("table_full", dict(B=4, L=1, Hq=8, Hkv=2, d=64, P=16, grow_frac=1.0, ctx=(60, 70), max_pages=6)),
+    # the pages' operating point: KV block 256, p 0.99, quota 64
+    ("paper_p256", dict(B=6, L=2, Hq=32, Hkv=8, d=128, P=256, ctx=(600, 4000), grow_frac=0.5,
+                        params=dict(SW.PARAMS_PAPER))),
+    ("p256_cow", dict(B=6, L=1, Hq=8, Hkv=2, d=64, P=256, grow_frac=0.2, prefix_groups=2, prefix_pages=2,
+                      ctx=(300, 1500), spare_pages=12, params=dict(SW.PARAMS_PAPER))),
+    ("p128_f32", dict(B=4, L=2, Hq=8, Hkv=2, d=128, P=128, dtype="f32", ctx=(100, 2000))),
 ]
 
 
