@@ -26,11 +26,17 @@ __device__ __forceinline__ float ord_key_inv(uint32_t k) {
 }
 
 // exp(y) for y <= 0 as a 2^-40 fixed-point integer, truncated: exact integer sums
-// make the softmax masses and their totals independent of summation order.
+// make the softmax masses and their totals independent of summation order.  The
+// hardware exp2 is used directly (results below 2^-40 truncate to 0 anyway, so its
+// handling of tiny results does not matter); floor(e * 2^40) is assembled from the
+// integer and fractional parts of e * 2^8, both exact in float32.
 constexpr float kMassScale = 1099511627776.0f;  // 2^40
 __device__ __forceinline__ uint64_t fixed_mass(float y) {
-  const float e = exp2f(y * 1.4426950408889634f);
-  return (uint64_t)(e * kMassScale);
+  const float e = __builtin_amdgcn_exp2f(y * 1.4426950408889634f);
+  const float h = e * 256.0f;                                   // in [0, 256]
+  const uint32_t hi = (uint32_t)h;
+  const uint32_t lo = (uint32_t)((h - (float)hi) * 4294967296.0f);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Block-wide exclusive prefix sum for blockDim.x == 256; returns the exclusive prefix of

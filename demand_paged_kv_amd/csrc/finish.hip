@@ -6,12 +6,12 @@
 // One 256-thread block per (entry, layer, KV head) unit, two reads of the unit's logits
 // ([n][8] float32, token-major, written by the logit kernel with each row's max M):
 //
-//   read 1  x = M - l >= 0 for every element of the 8 rows.  Elements with x < 255/16
-//           add their softmax mass exp(-x) (2^-40 fixed point, one 64-bit LDS atomic)
-//           to one of 255 bins of width 1/16; the rest add it to a per-thread tail sum.
+//   read 1  x = M - l >= 0 for every element of the 8 rows.  Each element adds its
+//           softmax mass exp(-x) (2^-40 fixed point, one 64-bit LDS atomic) to one of
+//           255 bins of width 1/16, or to bin 255 (the tail) when x >= 255/16.
 //           Integer sums make the normaliser Z exact and order-independent.  Walking
 //           the bins from x = 0 (largest probabilities) gives the bin b* where the mass
-//           reaches T = ceil(top_p * Z) -- or the tail, if the bins never reach it.
+//           reaches T = ceil(top_p * Z).
 //   read 2  per row: elements above b* are counted in registers, the elements of b* are
 //           appended to an LDS buffer (its size is bounded from the bin's mass: every
 //           element of bin b carries at least the mass of x = (b+1)/16); in the same
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
   __shared__ float cand[kCandCap];
   __shared__ u64 kbuf[kKeepCap];
   __shared__ float s_M[kDists], s_iz[kDists];
-  __shared__ u64 s_tail[kDists], s_T[kDists], s_above[kDists], s_Z[kDists];
+  __shared__ u64 s_T[kDists], s_above[kDists], s_Z[kDists];
   __shared__ uint32_t s_above_cnt[kDists], s_red[8];
   __shared__ int s_mode[kDists], s_bin[kDists], s_off[kDists], s_fill[kDists], s_ub[kDists], s_W[kDists];
   __shared__ int s_kcount;
@@ -322,54 +322,49 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
     return;
   }
 
-  // ---- read 1: binned masses and the tail mass
+  // ---- read 1: binned masses (bin 255 collects the tail)
   for (int i = tid; i < kDists * 256; i += 256) (&ms[0][0])[i] = 0;
   if (tid < kDists) {
     s_M[tid] = a.sp.stats[widx(tid) * 2];
-    s_tail[tid] = 0;
     s_above_cnt[tid] = 0;
   }
   __syncthreads();
   float M[kDists];
 #pragma unroll
   for (int k = 0; k < kDists; ++k) M[k] = s_M[k];
-  u64 tail[kDists];
+  {
+    float4 nlo[2], nhi[2];
+    auto fetch = [&](int i0) {
 #pragma unroll
-  for (int k = 0; k < kDists; ++k) tail[k] = 0;
-  for (int i0 = tid; i0 < n; i0 += 512) {
-    float v[2][kDists];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int i = i0 + 256 * t;
-      float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
-      if (i < n) {
-        lo = *reinterpret_cast<const float4*>(x + (int64_t)i * kDists);
-        hi = *reinterpret_cast<const float4*>(x + (int64_t)i * kDists + 4);
+      for (int t = 0; t < 2; ++t) {
+        const int i = i0 + 256 * t;
+        nlo[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+        nhi[t] = nlo[t];
+        if (i < n) {
+          nlo[t] = *reinterpret_cast<const float4*>(x + (int64_t)i * kDists);
+          nhi[t] = *reinterpret_cast<const float4*>(x + (int64_t)i * kDists + 4);
+        }
       }
-      v[t][0] = lo.x; v[t][1] = lo.y; v[t][2] = lo.z; v[t][3] = lo.w;
-      v[t][4] = hi.x; v[t][5] = hi.y; v[t][6] = hi.z; v[t][7] = hi.w;
-    }
+    };
+    fetch(tid);
+    for (int i0 = tid; i0 < n; i0 += 512) {
+      float v[2][kDists];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (i0 + 256 * t >= n) break;
+      for (int t = 0; t < 2; ++t) {
+        v[t][0] = nlo[t].x; v[t][1] = nlo[t].y; v[t][2] = nlo[t].z; v[t][3] = nlo[t].w;
+        v[t][4] = nhi[t].x; v[t][5] = nhi[t].y; v[t][6] = nhi[t].z; v[t][7] = nhi[t].w;
+      }
+      if (i0 + 512 < n) fetch(i0 + 512);
 #pragma unroll
-      for (int k = 0; k < kDists; ++k) {
-        const float xv = M[k] - v[t][k];
-        const u64 q = fixed_mass(-xv);
-        const int bin = x_bin(xv);
-        if (bin < kXBins)
-          atomicAdd(&ms[k][bin], q);
-        else
-          tail[k] += q;
+      for (int t = 0; t < 2; ++t) {
+        if (i0 + 256 * t >= n) break;
+#pragma unroll
+        for (int k = 0; k < kDists; ++k) {
+          const float xv = M[k] - v[t][k];
+          atomicAdd(&ms[k][x_bin(xv)], fixed_mass(-xv));
+        }
       }
     }
-  }
-#pragma unroll
-  for (int k = 0; k < kDists; ++k) {
-    u64 t = tail[k];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
-    if (lane == 0) atomicAdd(&s_tail[k], t);
   }
   __syncthreads();
 
@@ -379,12 +374,11 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
     u64 ls = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) ls += ms[k][4 * lane + q];
-    u64 tot_bins = 0;
-    wave_exscan_u64(ls, lane, &tot_bins);
-    const u64 Z = tot_bins + s_tail[k];
+    u64 Z = 0;
+    wave_exscan_u64(ls, lane, &Z);
     u64 T = 0;
     int mode = MODE_LDS, W = 0, chosen = kXBins;
-    u64 mb = tot_bins;
+    u64 mb = 0;
     uint32_t cb = 0;
     if (a.top_p >= 1.0f) {
       mode = MODE_DONE;
@@ -396,10 +390,11 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
         W = 1;
       }
     }
-    if (mode == MODE_LDS && !wave_find_crossing<false>(nullptr, &ms[k][0], 0, 0, T, lane, &chosen, &mb, &cb)) {
-      chosen = kXBins;  // crossing in the tail: every bin lies above it
-      mb = tot_bins;
-      mode = MODE_GLOBAL;
+    if (mode == MODE_LDS) {
+      // T <= Z, so some bin reaches it; a crossing in the tail bin (only a near-tie
+      // allows it) is refined by the block from global memory
+      wave_find_crossing<false>(nullptr, &ms[k][0], 0, 0, T, lane, &chosen, &mb, &cb);
+      if (chosen == kXBins) mode = MODE_GLOBAL;
     }
     if (lane == 0) {
       s_mode[k] = mode;
@@ -457,13 +452,20 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
     iz[k] = s_iz[k];
     above[k] = 0;
   }
+  float4 nlo = make_float4(0.f, 0.f, 0.f, 0.f), nhi = nlo;
+  if (tid < n) {
+    nlo = *reinterpret_cast<const float4*>(x + (int64_t)tid * kDists);
+    nhi = *reinterpret_cast<const float4*>(x + (int64_t)tid * kDists + 4);
+  }
   for (int base = 0; base < n; base += 256) {
     const int i = base + tid;
+    const float v8[kDists] = {nlo.x, nlo.y, nlo.z, nlo.w, nhi.x, nhi.y, nhi.z, nhi.w};
+    if (i + 256 < n) {
+      nlo = *reinterpret_cast<const float4*>(x + (int64_t)(i + 256) * kDists);
+      nhi = *reinterpret_cast<const float4*>(x + (int64_t)(i + 256) * kDists + 4);
+    }
     if (i < n) {
-      const float4 lo = *reinterpret_cast<const float4*>(x + (int64_t)i * kDists);
-      const float4 hi = *reinterpret_cast<const float4*>(x + (int64_t)i * kDists + 4);
-      const float v8[kDists] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      float imp = 0.f;
+      float imp = 0.f;  // slot importance: max over rows of exp(l - M) / Z
 #pragma unroll
       for (int k = 0; k < kDists; ++k) {
         const float v = v8[k];
@@ -474,7 +476,7 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
           const int p = atomicAdd(&s_fill[k], 1);
           if (p < bub[k]) cand[boff[k] + p] = v;  // a count beyond the bound sends the row to the block path
         }
-        imp = fmaxf(imp, exp2f(-xv * kLog2e) * iz[k]);
+        imp = fmaxf(imp, exp2f(-xv * kLog2e) * iz[k]);  // keeps tiny results (denormals) ordered
       }
       if (E > 0 && i < cand_slots) {
         const u64 key = ((u64)__float_as_uint(imp) << 32) | (uint32_t)i;

@@ -85,46 +85,46 @@ __global__ __launch_bounds__(1024) void plan_kernel(ScanArgs a) {
 }
 
 // ----------------------------------------------------------------------------- logits
+// 16 lanes share a token row: lane j (0..15) owns the D/16 contiguous elements
+// [j*D/16, (j+1)*D/16), so one wave step covers 4 tokens of one page.
+constexpr int kTokPerStep = 4;
+#ifndef GP_SCAN_BATCH
+#define GP_SCAN_BATCH 8
+#endif
+constexpr int kScanBatch = GP_SCAN_BATCH;  // steps whose loads are in flight together
+
 template <bool BF16, int D>
-struct Chunk;  // 2 x (D/16) elements of one row, as raw bits
+struct Chunk;  // the D/16 elements a lane owns in one row, as raw bits
 
 template <>
-struct Chunk<true, 128> {  // 2 x 8 bf16 = 2 x 16 B
-  uint4 c0, c1;
+struct Chunk<true, 128> {  // 8 bf16 = 16 B
+  uint4 c;
 };
 template <>
-struct Chunk<true, 64> {  // 2 x 4 bf16 = 2 x 8 B
-  uint2 c0, c1;
+struct Chunk<true, 64> {  // 4 bf16 = 8 B
+  uint2 c;
 };
 template <>
-struct Chunk<false, 64> {  // 2 x 4 f32 = 2 x 16 B
-  uint4 c0, c1;
+struct Chunk<false, 64> {  // 4 f32 = 16 B
+  uint4 c;
 };
 template <>
-struct Chunk<false, 128> {  // 2 x 8 f32 = 2 x 32 B
-  uint4 c0, c0b, c1, c1b;
+struct Chunk<false, 128> {  // 8 f32 = 32 B
+  uint4 c, c2;
 };
 
 template <bool BF16, int D>
 __device__ __forceinline__ void load_chunk(Chunk<BF16, D>& c, const char* row, int j) {
-  constexpr int W = D / 16;
+  constexpr int EL = D / 16;
   constexpr int E = BF16 ? 2 : 4;
-  const char* p0 = row + (size_t)j * W * E;
-  const char* p1 = row + (size_t)(D / 2 + j * W) * E;
-  if constexpr (BF16 && D == 128) {
-    c.c0 = *reinterpret_cast<const uint4*>(p0);
-    c.c1 = *reinterpret_cast<const uint4*>(p1);
-  } else if constexpr (BF16 && D == 64) {
-    c.c0 = *reinterpret_cast<const uint2*>(p0);
-    c.c1 = *reinterpret_cast<const uint2*>(p1);
-  } else if constexpr (!BF16 && D == 64) {
-    c.c0 = *reinterpret_cast<const uint4*>(p0);
-    c.c1 = *reinterpret_cast<const uint4*>(p1);
+  const char* p = row + (size_t)j * EL * E;
+  if constexpr (BF16 && D == 64) {
+    c.c = *reinterpret_cast<const uint2*>(p);
+  } else if constexpr (!BF16 && D == 128) {
+    c.c = *reinterpret_cast<const uint4*>(p);
+    c.c2 = *reinterpret_cast<const uint4*>(p + 16);
   } else {
-    c.c0 = *reinterpret_cast<const uint4*>(p0);
-    c.c0b = *reinterpret_cast<const uint4*>(p0 + 16);
-    c.c1 = *reinterpret_cast<const uint4*>(p1);
-    c.c1b = *reinterpret_cast<const uint4*>(p1 + 16);
+    c.c = *reinterpret_cast<const uint4*>(p);
   }
 }
 
@@ -135,61 +135,53 @@ __device__ __forceinline__ void unpack_bf16x2(uint32_t w, float& lo, float& hi) 
 
 template <bool BF16, int D>
 __device__ __forceinline__ void unpack_chunk(const Chunk<BF16, D>& c, float* kf) {
-  constexpr int W = D / 16;
   if constexpr (BF16 && D == 128) {
-    const uint32_t a[4] = {c.c0.x, c.c0.y, c.c0.z, c.c0.w};
-    const uint32_t b[4] = {c.c1.x, c.c1.y, c.c1.z, c.c1.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      unpack_bf16x2(a[i], kf[2 * i], kf[2 * i + 1]);
-      unpack_bf16x2(b[i], kf[W + 2 * i], kf[W + 2 * i + 1]);
-    }
+    unpack_bf16x2(c.c.x, kf[0], kf[1]);
+    unpack_bf16x2(c.c.y, kf[2], kf[3]);
+    unpack_bf16x2(c.c.z, kf[4], kf[5]);
+    unpack_bf16x2(c.c.w, kf[6], kf[7]);
   } else if constexpr (BF16 && D == 64) {
-    unpack_bf16x2(c.c0.x, kf[0], kf[1]);
-    unpack_bf16x2(c.c0.y, kf[2], kf[3]);
-    unpack_bf16x2(c.c1.x, kf[W + 0], kf[W + 1]);
-    unpack_bf16x2(c.c1.y, kf[W + 2], kf[W + 3]);
+    unpack_bf16x2(c.c.x, kf[0], kf[1]);
+    unpack_bf16x2(c.c.y, kf[2], kf[3]);
   } else if constexpr (!BF16 && D == 64) {
-    kf[0] = __uint_as_float(c.c0.x);
-    kf[1] = __uint_as_float(c.c0.y);
-    kf[2] = __uint_as_float(c.c0.z);
-    kf[3] = __uint_as_float(c.c0.w);
-    kf[W + 0] = __uint_as_float(c.c1.x);
-    kf[W + 1] = __uint_as_float(c.c1.y);
-    kf[W + 2] = __uint_as_float(c.c1.z);
-    kf[W + 3] = __uint_as_float(c.c1.w);
+    kf[0] = __uint_as_float(c.c.x);
+    kf[1] = __uint_as_float(c.c.y);
+    kf[2] = __uint_as_float(c.c.z);
+    kf[3] = __uint_as_float(c.c.w);
   } else {
-    const uint32_t a[8] = {c.c0.x, c.c0.y, c.c0.z, c.c0.w, c.c0b.x, c.c0b.y, c.c0b.z, c.c0b.w};
-    const uint32_t b[8] = {c.c1.x, c.c1.y, c.c1.z, c.c1.w, c.c1b.x, c.c1b.y, c.c1b.z, c.c1b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      kf[i] = __uint_as_float(a[i]);
-      kf[W + i] = __uint_as_float(b[i]);
-    }
+    kf[0] = __uint_as_float(c.c.x);
+    kf[1] = __uint_as_float(c.c.y);
+    kf[2] = __uint_as_float(c.c.z);
+    kf[3] = __uint_as_float(c.c.w);
+    kf[4] = __uint_as_float(c.c2.x);
+    kf[5] = __uint_as_float(c.c2.y);
+    kf[6] = __uint_as_float(c.c2.z);
+    kf[7] = __uint_as_float(c.c2.w);
   }
 }
 
-// Summary index held in register slot i by lane j of a token group: slots 0..3 hold
+// Summary index held in register slot i by lane j of an 8-lane group: slots 0..3 hold
 // j^i and slots 4..7 hold j^7^i, so that the reduce steps (pairs j<->j^7 by half-row
 // mirror, then j<->j^2, then j<->j^1) always add a partner's slot holding the same
 // summary and lane j finishes with summary j.
 __device__ __forceinline__ int slot_dist(int j, int i) { return i < 4 ? (j ^ i) : (j ^ 7 ^ (i - 4)); }
 
-constexpr int kPtCache = 4096;  // page-table entries of one request cached in LDS
+constexpr int kDppRowRor8 = 0x128;  // lane i <- lane (i + 8) mod 16 within each row of 16
 
-// One step = 8 tokens of one page.  Accumulate the 8 scores of this lane's token slice
-// and transpose-reduce them so that lane j of each 8-lane group holds summary j.
+// One step = 4 tokens of one page.  Accumulate the 8 scores of this lane's slice of its
+// token, transpose-reduce them within each 8-lane half (lane j&7 ends with summary j&7)
+// and add the other half of the row.
 template <bool BF16, int D>
-__device__ __forceinline__ float step_scores(const Chunk<BF16, D>& c, const float (&qr)[8][D / 8]) {
-  constexpr int W = D / 16;
-  float kf[2 * W];
+__device__ __forceinline__ float step_scores(const Chunk<BF16, D>& c, const float (&qr)[8][D / 16]) {
+  constexpr int EL = D / 16;
+  float kf[EL];
   unpack_chunk<BF16, D>(c, kf);
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float s = 0.f;
 #pragma unroll
-    for (int e = 0; e < 2 * W; ++e) s = __builtin_fmaf(qr[i][e], kf[e], s);
+    for (int e = 0; e < EL; ++e) s = __builtin_fmaf(qr[i][e], kf[e], s);
     acc[i] = s;
   }
 #pragma unroll
@@ -197,64 +189,70 @@ __device__ __forceinline__ float step_scores(const Chunk<BF16, D>& c, const floa
 #pragma unroll
   for (int i = 0; i < 2; ++i) acc[i] += dpp_mov<kDppQuadXor2>(acc[i + 2]);
   acc[0] += dpp_mov<kDppQuadXor1>(acc[1]);
+  acc[0] += dpp_mov<kDppRowRor8>(acc[0]);
   return acc[0];
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, int U>
 __global__ __launch_bounds__(64) void logit_kernel(ScanArgs a) {
 #pragma clang fp contract(off)
-  constexpr int W = D / 16;
-  constexpr int U = 4;  // steps per batch of loads
+  constexpr int EL = D / 16;
   constexpr int E = BF16 ? 2 : 4;
-  __shared__ int s_pt[kPtCache];
+  constexpr int TS = kTokPerStep;
   const Geo& g = a.g;
   const int lane = threadIdx.x;
-  const int tl = lane >> 3;
-  const int j = lane & 7;
+  const int tl = lane >> 4;      // token of the step
+  const int j = lane & 15;       // element slice
+  const int js = lane & 7;       // summary this lane ends a step with
+#ifdef GP_SCAN_LAYER_MAJOR
+  const int per_layer = g.n_req * g.Hkv;
+  const int l = blockIdx.x / per_layer;
+  const int rem = blockIdx.x - l * per_layer;
+  const int rank = rem / g.Hkv;
+  const int kvh = rem - rank * g.Hkv;
+#else
   const int upr = g.L * g.Hkv;
   const int rank = blockIdx.x / upr;
   const int rem = blockIdx.x - rank * upr;
   const int l = rem / g.Hkv;
   const int kvh = rem - l * g.Hkv;
+#endif
   const int b = a.sp.order[rank];
   if (a.sp.flags[b]) return;
   const int n = a.sp.n_tok[b];
   const int r = g.req_ids[b];
-  const int32_t* ptg = g.page_table + (int64_t)r * g.max_pages;
-  const int npages = (n + g.P - 1) / g.P;
-  const bool cached = npages <= kPtCache;
-  if (cached)
-    for (int i = lane; i < npages; i += 64) s_pt[i] = ptg[i];
+  const int32_t* pt = g.page_table + (int64_t)r * g.max_pages;
 
-  // Rotate the 8 summaries to the request position and fold in 1/sqrt(d).
-  float qr[8][2 * W];
+  // Rotate the 8 summaries to the request position (rotate-half pairs c, c + D/2) and
+  // fold in 1/sqrt(d); lane j keeps elements [j*EL, (j+1)*EL) of each.
+  float qr[8][EL];
   const bool rope = a.rope_cos != nullptr;
   const int pos = rope ? min(max(a.pos[r], 0), a.rope_max_pos - 1) : 0;
-  float cs[W], sn[W];
+  const bool first_half = j * EL < D / 2;
+  const int c0 = (j * EL) & (D / 2 - 1);   // pair index of this lane's first element
+  float cs[EL], sn[EL];
 #pragma unroll
-  for (int e = 0; e < W; ++e) {
-    cs[e] = rope ? a.rope_cos[(int64_t)pos * (D / 2) + j * W + e] : 1.f;
-    sn[e] = rope ? a.rope_sin[(int64_t)pos * (D / 2) + j * W + e] : 0.f;
+  for (int e = 0; e < EL; ++e) {
+    cs[e] = rope ? a.rope_cos[(int64_t)pos * (D / 2) + c0 + e] : 1.f;
+    sn[e] = rope ? a.rope_sin[(int64_t)pos * (D / 2) + c0 + e] : 0.f;
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int dist = slot_dist(j, i);
+    const int dist = slot_dist(js, i);
     const float* s = ((dist & 1) ? a.sum_l : a.sum_s) +
                      (((int64_t)r * g.L + l) * g.Hq + kvh * kGroup + (dist >> 1)) * D;
 #pragma unroll
-    for (int e = 0; e < W; ++e) {
-      const float x1 = s[j * W + e];
-      const float x2 = s[D / 2 + j * W + e];
-      qr[i][e] = (x1 * cs[e] - x2 * sn[e]) * a.scale;
-      qr[i][W + e] = (x2 * cs[e] + x1 * sn[e]) * a.scale;
+    for (int e = 0; e < EL; ++e) {
+      const float x1 = s[c0 + e];
+      const float x2 = s[D / 2 + c0 + e];
+      qr[i][e] = first_half ? (x1 * cs[e] - x2 * sn[e]) * a.scale : (x2 * cs[e] + x1 * sn[e]) * a.scale;
     }
   }
-  __syncthreads();
-  const int* pt = cached ? s_pt : ptg;
 
   const int64_t unit_base =
       (a.sp.tok_off[b] * g.L * g.Hkv + (int64_t)(l * g.Hkv + kvh) * n) * kDists;
-  float* lg = a.sp.logits + unit_base + j + tl * kDists;  // token-major: [n][8]
+  float* lg = a.sp.logits + unit_base + js + tl * kDists;  // token-major: [n][8]
+  const bool writer = j < 8;
   const char* kb = reinterpret_cast<const char*>(g.k) + ((int64_t)l * g.s_layer + (int64_t)kvh * g.s_head) * E +
                    (int64_t)tl * g.s_tok * E;
   const int64_t page_bytes = g.s_page * E;
@@ -262,14 +260,15 @@ __global__ __launch_bounds__(64) void logit_kernel(ScanArgs a) {
   float m = -INFINITY;
 
   // Full batches of U steps, loads of the next batch issued before this one is reduced.
-  const int nfull = (n / (8 * U)) * (8 * U);
+  // Page index and in-page offset are wave-uniform, so page ids come in by scalar loads.
+  const int nfull = (n / (TS * U)) * (TS * U);
   int pj = 0, sub = 0;  // page index and in-page offset of the next step to load
   auto load_batch = [&](Chunk<BF16, D>(&c)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const char* row = kb + (int64_t)pt[pj] * page_bytes + (int64_t)sub * tok_bytes;
       load_chunk<BF16, D>(c[u], row, j);
-      sub += 8;
+      sub += TS;
       if (sub == g.P) {
         sub = 0;
         ++pj;
@@ -278,46 +277,45 @@ __global__ __launch_bounds__(64) void logit_kernel(ScanArgs a) {
   };
   Chunk<BF16, D> cur[U], nxt[U];
   if (nfull > 0) load_batch(cur);
-  for (int t0 = 0; t0 < nfull; t0 += 8 * U) {
-    if (t0 + 8 * U < nfull) load_batch(nxt);
+  for (int t0 = 0; t0 < nfull; t0 += TS * U) {
+    if (t0 + TS * U < nfull) load_batch(nxt);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float x = step_scores<BF16, D>(cur[u], qr);
-      lg[(int64_t)(t0 + 8 * u) * kDists] = x;
+      if (writer) lg[(int64_t)(t0 + TS * u) * kDists] = x;
       m = fmaxf(m, x);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) cur[u] = nxt[u];
   }
   // Tail: single steps, the last one possibly partial.
-  for (int t0 = nfull; t0 < n; t0 += 8) {
+  for (int t0 = nfull; t0 < n; t0 += TS) {
     Chunk<BF16, D> c{};
     const bool ok = t0 + tl < n;
     if (ok) load_chunk<BF16, D>(c, kb + (int64_t)pt[pj] * page_bytes + (int64_t)sub * tok_bytes, j);
-    sub += 8;
+    sub += TS;
     if (sub == g.P) {
       sub = 0;
       ++pj;
     }
     const float x = step_scores<BF16, D>(c, qr);
     if (ok) {
-      lg[(int64_t)t0 * kDists] = x;
+      if (writer) lg[(int64_t)t0 * kDists] = x;
       m = fmaxf(m, x);
     }
   }
-  m = fmaxf(m, __shfl_xor(m, 8, 64));
   m = fmaxf(m, __shfl_xor(m, 16, 64));
   m = fmaxf(m, __shfl_xor(m, 32, 64));
-  if (tl == 0) {
-    const int h = kvh * kGroup + (j >> 1);
-    const int64_t si = ((((int64_t)b * g.L + l) * g.Hq + h) * 2 + (j & 1)) * 2;
+  if (lane < 8) {
+    const int h = kvh * kGroup + (js >> 1);
+    const int64_t si = ((((int64_t)b * g.L + l) * g.Hq + h) * 2 + (js & 1)) * 2;
     a.sp.stats[si] = m;
   }
 }
 
 template <bool BF16, int D>
 hipError_t launch_logits(const ScanArgs& a, int64_t units, hipStream_t st) {
-  hipLaunchKernelGGL((logit_kernel<BF16, D>), dim3((unsigned)units), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((logit_kernel<BF16, D, kScanBatch>), dim3((unsigned)units), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
