@@ -51,12 +51,13 @@ def parse():
                     help="layer-tokens of oracle work in the CPU baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 4 GiB device copy (HBM counter calibration)")
-    ap.add_argument("--workload", choices=("boundary_sweep", "decode_loop", "prefix_share"),
+    ap.add_argument("--workload", choices=("boundary_sweep", "decode_loop", "prefix_share", "policies"),
                     default="boundary_sweep",
                     help="boundary_sweep (default, the headline line); decode_loop (the 36-layer decode "
                          "loop: 128 requests x 4096 steps) or prefix_share (256 requests x 36 layers, page "
-                         "32, shared 2048-token prefixes, pool at 80%% of demand; one shot), each reported "
-                         "on its own line")
+                         "32, shared 2048-token prefixes, pool at 80%% of demand; one shot) or policies (the "
+                         "decode loop under each decision policy: grow ratios, and the signal's rank "
+                         "correlation with the later working set), each reported on its own line")
     ap.add_argument("--decode-steps", type=int, default=4096)
     ap.add_argument("--paper", action="store_true",
                     help="boundary sweep at the pages' operating point (KV block 256, p 0.99, quota 64), "
@@ -94,6 +95,9 @@ def main():
         return
     if args.workload == "prefix_share":
         prefix_share(args)
+        return
+    if args.workload == "policies":
+        policies(args)
         return
     import numpy as np
     import torch
@@ -317,6 +321,85 @@ def decode_loop(args):
         "grows": int(grows.sum().item()),
         "counters": c,
     }
+    print(json.dumps(result), flush=True)
+
+
+def policies(args):
+    """The decode loop (128 requests x 36 layers from 1024-token prompts, --decode-steps
+    steps) under each decision policy: GrowPage's own rule, RANDOM at GrowPage's measured
+    grow ratio (frequency-matched), INVERSE and ALWAYS_COMPACT.  Reports grow ratios and
+    pages in use at the end.  For GrowPage's run it also reports how the boundary signal
+    delta_t ranks against the change of the recent working set over the next h boundaries,
+    sum W_S(t+h) - sum W_L(t) (Spearman rho and sign agreement) -- a model-free analogue of
+    the pages' demand-prediction check (GrowPage review, "Key claims", Fig 6)."""
+    import numpy as np
+    import torch
+    from scipy.stats import spearmanr
+
+    from demand_paged_kv_amd import binding as Bd
+    from demand_paged_kv_amd.engine import BoundaryEngine
+    from synth.decode_loop import DecodeLoopGen, DecodeSpec
+
+    Bd.load()
+    steps = min(args.decode_steps, 2048)
+    out = {}
+    grow_ratio = None
+    sig = None
+    for policy in ("growpage", "random", "inverse", "always_compact"):
+        spec = DecodeSpec(steps=steps)
+        gen = DecodeLoopGen(spec, "cuda")
+        st = gen.initial_state()
+        eng = BoundaryEngine(st, spec.B, spec.B * (spec.prompt + spec.steps + spec.P),
+                             Bd.params_from(spec.params))
+        req = torch.arange(spec.B, dtype=torch.int32, device="cuda")
+        rng = np.random.default_rng(spec.seed + 7)
+        u = torch.zeros(spec.B, dtype=torch.float32, device="cuda")
+        eng.set_policy(policy, u, grow_ratio or 0.0)
+        grows = denied = boundaries = 0
+        ws_s, ws_l, deltas = [], [], []
+        t0 = time.time()
+        for t in range(spec.steps):
+            q, k, v = gen.step()
+            st.pos.fill_(spec.prompt + t)
+            boundary = (t + 1) % spec.P == 0
+            if boundary:
+                u.copy_(torch.from_numpy(rng.random(spec.B).astype(np.float32)))
+            o = eng.decode_step(q, k, v, req, req if boundary else None)
+            if boundary:
+                boundaries += 1
+                c = o.counters.cpu().numpy()
+                grows += int(c[0])
+                denied += int(c[2])
+                if policy == "growpage":
+                    w = o.ws[: spec.B].to(torch.int64).sum(dim=(1, 2)).cpu().numpy()     # [B][2]
+                    ws_s.append(w[:, 0])
+                    ws_l.append(w[:, 1])
+                    deltas.append(o.delta[: spec.B].cpu().numpy().astype(np.int64))
+        torch.cuda.synchronize()
+        pages = int(st.n_alloc[: spec.B].sum().item()) + spec.B
+        ratio = grows / (boundaries * spec.B)
+        out[policy] = {"grow_ratio": round(ratio, 4), "grows": grows, "grow_denied": denied,
+                       "pages_in_use_end": pages, "boundaries": boundaries,
+                       "wall_s": round(time.time() - t0, 2)}
+        log(f"policy {policy}: grow ratio {ratio:.4f}, pages {pages}")
+        if policy == "growpage":
+            grow_ratio = ratio
+            S, Lg, D = np.array(ws_s), np.array(ws_l), np.array(deltas)             # [boundaries][B]
+            sig = {}
+            for h in (1, 2, 4, 8):
+                fut = (S[h:] - Lg[:-h]).ravel()
+                dd = D[:-h].ravel()
+                rho = spearmanr(dd, fut).correlation
+                agree = float(np.mean(np.sign(dd) == np.sign(fut)))
+                sig[f"h{h}"] = {"spearman": round(float(rho), 4), "sign_agreement": round(agree, 4),
+                                "pairs": int(dd.size)}
+        del eng, st, gen
+        torch.cuda.empty_cache()
+    result = {"metric": "decision-policy grow ratios and boundary-signal rank correlation (decode loop)",
+              "config": {"workload": f"decode_loop: 128 requests x 36 layers, page 16, 1024-token prompts, "
+                                     f"{steps} decode steps"},
+              "random_grow_prob": round(grow_ratio, 4), "policies": out, "signal_vs_future": sig,
+              "data": "synthetic"}
     print(json.dumps(result), flush=True)
 
 

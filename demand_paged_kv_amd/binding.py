@@ -24,8 +24,10 @@ GP_NUM_COUNTERS = len(COUNTER_NAMES)
 
 EXPORTED = ("gp_abi_version", "gp_status_string", "gp_last_hip_error_string", "gp_update_summaries",
             "gp_scratch_bytes",
-            "gp_boundary_scan", "gp_decide", "gp_compact", "gp_compact_prepare", "gp_compact_move",
-            "gp_append_kv")
+            "gp_boundary_scan", "gp_decide", "gp_decide_policy", "gp_compact", "gp_compact_prepare",
+            "gp_compact_move", "gp_append_kv")
+# decision policies (gp_decide_policy)
+POLICIES = {"growpage": 0, "random": 1, "inverse": 2, "always_compact": 3}
 
 
 class GrowPageError(RuntimeError):
@@ -84,6 +86,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gp_decide.restype = i32
     lib.gp_decide.argtypes = [P, P, i32, i32, i32, i32, ctypes.POINTER(Params),
                               ctypes.POINTER(Pages), P, P, P, P, P]
+    lib.gp_decide_policy.restype = i32
+    lib.gp_decide_policy.argtypes = [P, P, i32, i32, i32, i32, ctypes.POINTER(Params), i32, P,
+                                     ctypes.c_float, ctypes.POINTER(Pages), P, P, P, P, P]
     lib.gp_compact.restype = i32
     lib.gp_compact.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Pages), P, P, i32,
                                ctypes.POINTER(Params), P, P, P, P, sz, i64, P]
@@ -176,6 +181,15 @@ def decide(ws, req_ids, n_req, L, Hq, P, prm: Params, pages: Pages, decision_out
                           ctypes.byref(prm), ctypes.byref(pages), _ptr(decision_out),
                           _ptr(delta_out), _ptr(status_out), _ptr(counters_out), _stream(stream))
     _check(st, "gp_decide")
+
+
+def decide_policy(ws, req_ids, n_req, L, Hq, P, prm: Params, policy: str, rand_u, grow_prob,
+                  pages: Pages, decision_out, delta_out, status_out, counters_out=None, stream=None):
+    st = load().gp_decide_policy(_ptr(ws), _ptr(req_ids), int(n_req), int(L), int(Hq), int(P),
+                                 ctypes.byref(prm), POLICIES[policy], _ptr(rand_u), float(grow_prob),
+                                 ctypes.byref(pages), _ptr(decision_out), _ptr(delta_out),
+                                 _ptr(status_out), _ptr(counters_out), _stream(stream))
+    _check(st, "gp_decide_policy")
 
 
 def compact(kv: KV, pages: Pages, req_ids, decision, n_req, prm: Params, evicted_out, status_out,

@@ -151,8 +151,26 @@ gp_status gp_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_req, in
   if (n_req < 0 || n_req > pages->max_req || L <= 0 || Hq <= 0 || P <= 0) return GP_ERR_INVALID;
   if (n_req == 0) return GP_OK;
   if (!ws || !req_ids || !decision_out || !delta_out || !status_out) return GP_ERR_INVALID;
-  return from_hip(launch_decide(ws, req_ids, n_req, L, Hq, params->tau, *pages, P, decision_out,
-                                delta_out, status_out, counters_out, (hipStream_t)stream));
+  return from_hip(launch_decide(ws, req_ids, n_req, L, Hq, params->tau, *pages, P, GP_POLICY_GROWPAGE,
+                                nullptr, 0.f, decision_out, delta_out, status_out, counters_out,
+                                (hipStream_t)stream));
+}
+
+gp_status gp_decide_policy(const int32_t* ws, const int32_t* req_ids, int32_t n_req, int32_t L,
+                           int32_t Hq, int32_t P, const gp_params* params, int32_t policy,
+                           const float* rand_u, float grow_prob, const gp_pages* pages,
+                           uint8_t* decision_out, int32_t* delta_out, int32_t* status_out,
+                           int32_t* counters_out, void* stream) {
+  if (gp_status s = check_pages(pages, true)) return s;
+  if (gp_status s = check_params(params)) return s;
+  if (policy < GP_POLICY_GROWPAGE || policy > GP_POLICY_ALWAYS_COMPACT) return GP_ERR_INVALID;
+  if (n_req < 0 || n_req > pages->max_req || L <= 0 || Hq <= 0 || P <= 0) return GP_ERR_INVALID;
+  if (n_req == 0) return GP_OK;
+  if (!ws || !req_ids || !decision_out || !delta_out || !status_out) return GP_ERR_INVALID;
+  if (policy == GP_POLICY_RANDOM && !rand_u) return GP_ERR_INVALID;
+  return from_hip(launch_decide(ws, req_ids, n_req, L, Hq, params->tau, *pages, P, policy, rand_u,
+                                grow_prob, decision_out, delta_out, status_out, counters_out,
+                                (hipStream_t)stream));
 }
 
 namespace {

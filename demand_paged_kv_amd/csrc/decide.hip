@@ -2,7 +2,9 @@
 // working set triggers allocation of one extra physical page, otherwise compact; FAQ
 // "Is GrowPage's code available?": demand threshold tau 0).
 //
-// delta_b = sum over layers and query heads of (W_short - W_long); grow iff delta > tau.
+// delta_b = sum over layers and query heads of (W_short - W_long); grow iff delta > tau
+// (or, for the ablation policies the pages compare: iff -delta > tau, iff a uniform draw
+// falls below a grow probability, or never).
 // Grows pop the device free stack in batch order: the eligible entries are ranked by a
 // block prefix sum and the first `free_top` of them receive free_stack[top-1-rank], so
 // page ids are deterministic without atomics.  One 1024-thread block: the batch is
@@ -16,7 +18,9 @@ namespace {
 struct DecideArgs {
   const int32_t* ws;
   const int32_t* req_ids;
-  int32_t n_req, L, Hq, tau, P;
+  int32_t n_req, L, Hq, tau, P, policy;
+  const float* rand_u;
+  float grow_prob;
   gp_pages pg;
   uint8_t* decision;
   int32_t* delta;
@@ -60,7 +64,12 @@ __global__ __launch_bounds__(1024) void decide_kernel(DecideArgs a) {
       const bool at = a.pg.fill[r] == a.P;
       if (over) st |= GP_REQ_OVERFLOW;
       if (!at) st |= GP_REQ_NOT_AT_BOUNDARY;
-      want = (!over && at && a.delta[b] > a.tau) ? 1 : 0;
+      const int d = a.delta[b];
+      bool grow = d > a.tau;
+      if (a.policy == GP_POLICY_INVERSE) grow = -(long long)d > a.tau;
+      else if (a.policy == GP_POLICY_RANDOM) grow = a.rand_u[b] < a.grow_prob;
+      else if (a.policy == GP_POLICY_ALWAYS_COMPACT) grow = false;
+      want = (!over && at && grow) ? 1 : 0;
       eligible = (want && A + 2 <= a.pg.max_pages) ? 1 : 0;
     }
     int total = 0;
@@ -98,10 +107,11 @@ __global__ __launch_bounds__(1024) void decide_kernel(DecideArgs a) {
 }  // namespace
 
 hipError_t launch_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_req, int32_t L,
-                         int32_t Hq, int32_t tau, const gp_pages& pg, int32_t P,
-                         uint8_t* decision, int32_t* delta, int32_t* status, int32_t* counters,
-                         hipStream_t st) {
-  DecideArgs a{ws, req_ids, n_req, L, Hq, tau, P, pg, decision, delta, status, counters};
+                         int32_t Hq, int32_t tau, const gp_pages& pg, int32_t P, int32_t policy,
+                         const float* rand_u, float grow_prob, uint8_t* decision, int32_t* delta,
+                         int32_t* status, int32_t* counters, hipStream_t st) {
+  DecideArgs a{ws, req_ids, n_req, L, Hq, tau, P, policy, rand_u, grow_prob, pg, decision, delta, status,
+               counters};
   hipLaunchKernelGGL(decide_kernel, dim3(1), dim3(1024), 0, st, a);
   return hipGetLastError();
 }

@@ -137,9 +137,9 @@ struct FinishArgs {
 hipError_t launch_finish(const FinishArgs& a, hipStream_t st);
 
 hipError_t launch_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_req, int32_t L,
-                         int32_t Hq, int32_t tau, const gp_pages& pg, int32_t P,
-                         uint8_t* decision, int32_t* delta, int32_t* status, int32_t* counters,
-                         hipStream_t st);
+                         int32_t Hq, int32_t tau, const gp_pages& pg, int32_t P, int32_t policy,
+                         const float* rand_u, float grow_prob, uint8_t* decision, int32_t* delta,
+                         int32_t* status, int32_t* counters, hipStream_t st);
 
 hipError_t launch_compact_prepare(const Geo& g, const gp_pages& pg, const ScratchPtrs& sp,
                                   const uint8_t* decision, int32_t* evicted_out,

@@ -85,6 +85,7 @@ class BoundaryEngine:
             counters=torch.zeros(B.GP_NUM_COUNTERS, dtype=torch.int32, device=dev),
         )
         self.max_batch = n
+        self.policy, self.rand_u, self.grow_prob = "growpage", None, 0.0
 
     def scan(self, req_ids: torch.Tensor, stream=None):
         st, o, nb = self.st, self.out, int(req_ids.numel())
@@ -96,8 +97,21 @@ class BoundaryEngine:
 
     def decide(self, req_ids: torch.Tensor, stream=None):
         st, o, nb = self.st, self.out, int(req_ids.numel())
-        B.decide(o.ws, req_ids, nb, st.L, st.Hq, st.P, self.prm, self.pages, o.decision, o.delta,
-                 o.status, o.counters, stream)
+        if self.policy == "growpage":
+            B.decide(o.ws, req_ids, nb, st.L, st.Hq, st.P, self.prm, self.pages, o.decision, o.delta,
+                     o.status, o.counters, stream)
+        else:
+            B.decide_policy(o.ws, req_ids, nb, st.L, st.Hq, st.P, self.prm, self.policy, self.rand_u,
+                            self.grow_prob, self.pages, o.decision, o.delta, o.status, o.counters,
+                            stream)
+
+    def set_policy(self, policy: str = "growpage", rand_u: Optional[torch.Tensor] = None,
+                   grow_prob: float = 0.0):
+        """Decision policy of later decide() calls; rand_u: [batch] float32 uniform draws
+        (device), read at the time of each decide() (policy "random" only)."""
+        assert policy in B.POLICIES
+        assert policy != "random" or (rand_u is not None and rand_u.dtype == torch.float32)
+        self.policy, self.rand_u, self.grow_prob = policy, rand_u, float(grow_prob)
 
     def compact(self, req_ids: torch.Tensor, stream=None):
         o, nb = self.out, int(req_ids.numel())

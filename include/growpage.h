@@ -181,6 +181,27 @@ gp_status gp_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_req, in
                     uint8_t* decision_out, int32_t* delta_out, int32_t* status_out,
                     int32_t* counters_out, void* stream);
 
+/* Decision policies the pages compare against GrowPage's own rule (GrowPage review,
+ * "Strengths", item "Frequency-matched causal ablations", Tables 8-9; FAQ "How does
+ * GrowPage differ from Zipage?" for the fixed budget). */
+typedef enum {
+  GP_POLICY_GROWPAGE = 0,        /* grow iff delta > tau (gp_decide)                         */
+  GP_POLICY_RANDOM = 1,          /* grow iff rand_u[b] < grow_prob (frequency-matched random) */
+  GP_POLICY_INVERSE = 2,         /* grow iff -delta > tau (signal direction reversed)        */
+  GP_POLICY_ALWAYS_COMPACT = 3   /* never grow (fixed per-request budget)                    */
+} gp_policy;
+
+/* gp_decide under a decision policy; everything but the grow/compact choice is as in
+ * gp_decide (delta_out is always the signal).  rand_u: device float32 [n_req] uniform
+ * draws in [0, 1), required for GP_POLICY_RANDOM and ignored otherwise; grow_prob: the
+ * grow probability of GP_POLICY_RANDOM.  Errors: GP_ERR_INVALID for an unknown policy,
+ * a missing rand_u, or the gp_decide conditions. */
+gp_status gp_decide_policy(const int32_t* ws, const int32_t* req_ids, int32_t n_req, int32_t L,
+                           int32_t Hq, int32_t P, const gp_params* params, int32_t policy,
+                           const float* rand_u, float grow_prob, const gp_pages* pages,
+                           uint8_t* decision_out, int32_t* delta_out, int32_t* status_out,
+                           int32_t* counters_out, void* stream);
+
 /* Compaction (GrowPage review, "Summary": compact within the current allocation by the
  * maximum of both temporal importance scores; abstract: prefix caching preserved).
  * For every batch entry with decision COMPACT and fill == P: selects the n - k evicted

@@ -165,6 +165,29 @@ def decide(ws: np.ndarray, wl: np.ndarray, tau: int) -> tuple:
     return delta, (DECISION_GROW if delta > tau else DECISION_COMPACT)
 
 
+POLICIES = ("growpage", "random", "inverse", "always_compact")
+
+
+def policy_decision(delta: int, tau: int, policy: str = "growpage", u: float = 0.0,
+                    grow_prob: float = 0.0) -> int:
+    """Grow or compact under the decision policies the pages compare [review, "Strengths",
+    item "Frequency-matched causal ablations" (Tables 8-9): RANDOM keeps GrowPage's grow
+    ratio without its signal, INVERSE reverses the signal's direction; FAQ "How does
+    GrowPage differ from Zipage?": a fixed per-request budget never grows].  Readings: growpage grows iff
+    delta > tau (R2); inverse grows iff -delta > tau; random grows iff the request's
+    uniform draw u (an input, float32) is below grow_prob (float32); always_compact
+    never grows."""
+    if policy == "growpage":
+        return DECISION_GROW if delta > tau else DECISION_COMPACT
+    if policy == "inverse":
+        return DECISION_GROW if -delta > tau else DECISION_COMPACT
+    if policy == "random":
+        return DECISION_GROW if np.float32(u) < np.float32(grow_prob) else DECISION_COMPACT
+    if policy == "always_compact":
+        return DECISION_COMPACT
+    raise ValueError(policy)
+
+
 def importance(a_group: np.ndarray) -> np.ndarray:
     """Max-of-both importance per slot [Summary: "maximum of both temporal importance
     scores"]; reading R5: max over the KV head's query heads and both summaries."""
@@ -300,13 +323,18 @@ def boundary_step(wl, sum_s: np.ndarray, sum_l: np.ndarray, params: dict) -> Ste
 
     ``wl`` carries the per-request stored rows and the page state (see synth.Workload);
     sum_s/sum_l [B][L][Hq][d] float32 are the summaries at the boundary.  Follows
-    [Summary] and [Abstract] under readings R1-R7.  Inputs are not modified.
+    [Summary] and [Abstract] under readings R1-R7.  Inputs are not modified.  Optional
+    params "policy", "rand_u" ([B] float32) and "grow_prob" select a decision policy
+    (policy_decision); the default is GrowPage's own rule.
     """
     B, L, Hq, Hkv, P = wl.B, wl.L, wl.Hq, wl.Hkv, wl.P
     G = Hq // Hkv
     p = float(np.float32(params["top_p"]))
     tau = int(params["tau"])
     n_local = int(params["n_local"])
+    policy = params.get("policy", "growpage")
+    rand_u = params.get("rand_u")
+    grow_prob = params.get("grow_prob", 0.0)
     W = np.zeros((B, L, Hq, 2), np.int64)
     Wlo, Whi = np.zeros_like(W), np.zeros_like(W)
     M = np.zeros((B, L, Hq, 2))
@@ -324,8 +352,11 @@ def boundary_step(wl, sum_s: np.ndarray, sum_l: np.ndarray, params: dict) -> Ste
         res = scan_request(wl.k_rows[b], wl.dtype, sum_s[b], sum_l[b], cr, sr, p, keep_logits=True)
         W[b], Wlo[b], Whi[b], M[b], Z[b], probs[b] = res
         delta[b], dlo[b], dhi[b] = delta_range(W[b], Wlo[b], Whi[b])
-        raw[b] = DECISION_GROW if delta[b] > tau else DECISION_COMPACT
-        amb[b] = (dlo[b] <= tau) and (dhi[b] > tau)
+        u = 0.0 if rand_u is None else float(rand_u[b])
+        raw[b] = policy_decision(int(delta[b]), tau, policy, u, grow_prob)
+        lo_d = policy_decision(int(dlo[b]), tau, policy, u, grow_prob)
+        hi_d = policy_decision(int(dhi[b]), tau, policy, u, grow_prob)
+        amb[b] = lo_d != hi_d
 
     table = wl.page_table.copy()
     A = wl.n_alloc.astype(np.int64).copy()

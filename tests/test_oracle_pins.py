@@ -465,3 +465,33 @@ def test_decode_compaction_keeps_a_stable_subset():
         kept = np.setdiff1d(np.arange((A + 1) * P), res.evicted[0][0, 0])
         assert np.array_equal(st.k_rows[0][0, 0], rows_seen[0, 0][kept])
         assert st.k_rows[0].shape[2] == A * P
+
+
+# ----------------------------------------------------------------------------- decision policies
+def test_policy_rules():
+    """The ablation policies as read: inverse grows iff -delta > tau, random iff its draw is
+    below the grow probability (strictly), always_compact never; ties compact throughout."""
+    for d in (-5, -1, 0, 1, 7):
+        for tau in (0, 2):
+            assert O.policy_decision(d, tau, "growpage") == (d > tau)
+            assert O.policy_decision(d, tau, "inverse") == (-d > tau)
+            assert O.policy_decision(d, tau, "always_compact") == O.DECISION_COMPACT
+    assert O.policy_decision(0, 0, "growpage") == O.policy_decision(0, 0, "inverse") == O.DECISION_COMPACT
+    for u, rho, want in ((0.0, 0.0, 0), (0.999, 1.0, 1), (0.3, 0.3, 0), (0.29, 0.3, 1)):
+        assert O.policy_decision(100, 0, "random", u, rho) == want
+    with pytest.raises(ValueError):
+        O.policy_decision(1, 0, "shrink")
+
+
+def test_boundary_step_follows_the_policy():
+    wl = SW.direct_case(seed=77, B=6, L=1, Hq=8, Hkv=2, d=64, P=16, grow_frac=0.5, spare_pages=64)
+    base = O.boundary_step(wl, wl.sum_s, wl.sum_l, wl.params)
+    assert 0 < base.decision.sum() < wl.B
+    inv = O.boundary_step(wl, wl.sum_s, wl.sum_l, dict(wl.params, policy="inverse"))
+    assert np.array_equal(inv.delta, base.delta)
+    assert np.array_equal(inv.decision, (-base.delta > 0).astype(inv.decision.dtype))
+    never = O.boundary_step(wl, wl.sum_s, wl.sum_l, dict(wl.params, policy="always_compact"))
+    assert never.decision.sum() == 0 and never.counters["compacts"] == wl.B
+    u = np.array([0.1, 0.9, 0.5, 0.2, 0.7, 0.05], np.float32)
+    rnd = O.boundary_step(wl, wl.sum_s, wl.sum_l, dict(wl.params, policy="random", rand_u=u, grow_prob=0.3))
+    assert np.array_equal(rnd.decision, (u < np.float32(0.3)).astype(rnd.decision.dtype))

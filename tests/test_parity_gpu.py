@@ -203,3 +203,23 @@ def test_planted_logits(name, fns, params):
     st, out, _ = run_step_gpu(wl)
     rep = compare_step(wl, np.arange(wl.B), st, out, res, wl.params["n_local"])
     _say(name, rep, res.counters, "W", res.W[:, 0, 0].tolist())
+
+
+@pytest.mark.parametrize("policy", ["growpage", "random", "inverse", "always_compact"])
+def test_decision_policies(policy):
+    """The ablation policies through gp_decide_policy, the rest of the batch as usual."""
+    from demand_paged_kv_amd import binding as Bd
+    from demand_paged_kv_amd.engine import BoundaryEngine
+    from synth import device as SD
+    wl = SW.direct_case(seed=911, B=10, L=2, Hq=32, Hkv=8, d=128, P=16, ctx=(100, 900), grow_frac=0.5,
+                        spare_pages=6)
+    u = np.random.default_rng(912).random(wl.B).astype(np.float32)
+    prm = dict(wl.params, policy=policy, rand_u=u, grow_prob=0.4)
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, prm)
+    _say(f"[policy] {policy}: decisions {res.decision.tolist()} status {res.status.tolist()}")
+    st = SD.upload(wl, "cuda")
+    eng = BoundaryEngine(st, wl.B, wl.total_tokens(), Bd.params_from(wl.params))
+    eng.set_policy(policy, torch.as_tensor(u, device="cuda"), 0.4)
+    out = eng.step(torch.arange(wl.B, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    compare_step(wl, np.arange(wl.B), st, out, res, wl.params["n_local"])
