@@ -82,6 +82,75 @@ __device__ __forceinline__ int block_exscan_1024(int v, int* tmp, int* total) {
   return base + x - v;
 }
 
+// ---- wave64 prefix scans and reductions on DPP lane moves (no LDS traffic).  Each
+// step moves a value within rows of 16 lanes (row_shr) or from the last lane of one row
+// to the following rows (row_bcast15 / row_bcast31); lanes a step does not write keep
+// the identity passed as `old`.  Call with all 64 lanes active.
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = dpp_u32<CTRL, ROW_MASK>(0u, (uint32_t)v);
+  const uint32_t hi = dpp_u32<CTRL, ROW_MASK>(0u, (uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive prefix sums over lanes 0..63.
+__device__ __forceinline__ uint32_t wave_incl_sum_u32(uint32_t x) {
+  x += dpp_u32<kDppRowShr1, 0xF>(0u, x);
+  x += dpp_u32<kDppRowShr2, 0xF>(0u, x);
+  x += dpp_u32<kDppRowShr4, 0xF>(0u, x);
+  x += dpp_u32<kDppRowShr8, 0xF>(0u, x);
+  x += dpp_u32<kDppRowBcast15, 0xA>(0u, x);
+  x += dpp_u32<kDppRowBcast31, 0xC>(0u, x);
+  return x;
+}
+__device__ __forceinline__ uint64_t wave_incl_sum_u64(uint64_t x) {
+  x += dpp_u64<kDppRowShr1, 0xF>(x);
+  x += dpp_u64<kDppRowShr2, 0xF>(x);
+  x += dpp_u64<kDppRowShr4, 0xF>(x);
+  x += dpp_u64<kDppRowShr8, 0xF>(x);
+  x += dpp_u64<kDppRowBcast15, 0xA>(x);
+  x += dpp_u64<kDppRowBcast31, 0xC>(x);
+  return x;
+}
+// Value of lane `lane` (wave-uniform) in every lane.
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int lane) {
+  return ((uint64_t)lane_u32((uint32_t)(v >> 32), lane) << 32) | lane_u32((uint32_t)v, lane);
+}
+// Minimum / maximum over the wave (prefix min/max, then lane 63).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  constexpr uint32_t I = 0xffffffffu;
+  x = min(x, dpp_u32<kDppRowShr1, 0xF>(I, x));
+  x = min(x, dpp_u32<kDppRowShr2, 0xF>(I, x));
+  x = min(x, dpp_u32<kDppRowShr4, 0xF>(I, x));
+  x = min(x, dpp_u32<kDppRowShr8, 0xF>(I, x));
+  x = min(x, dpp_u32<kDppRowBcast15, 0xA>(I, x));
+  x = min(x, dpp_u32<kDppRowBcast31, 0xC>(I, x));
+  return lane_u32(x, 63);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u32<kDppRowShr1, 0xF>(0u, x));
+  x = max(x, dpp_u32<kDppRowShr2, 0xF>(0u, x));
+  x = max(x, dpp_u32<kDppRowShr4, 0xF>(0u, x));
+  x = max(x, dpp_u32<kDppRowShr8, 0xF>(0u, x));
+  x = max(x, dpp_u32<kDppRowBcast15, 0xA>(0u, x));
+  x = max(x, dpp_u32<kDppRowBcast31, 0xC>(0u, x));
+  return lane_u32(x, 63);
+}
+
 __device__ __forceinline__ int wave_sum_int(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

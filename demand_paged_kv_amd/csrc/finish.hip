@@ -19,8 +19,8 @@
 //           buffer that keeps the n - k least important candidate slots (ties: older
 //           slot first) -- the slots a compaction evicts.
 //   refine  per row, an exact radix select over the b* elements only, weighted by the
-//           same fixed-point masses, starting at the highest key bit in which they
-//           differ: W = (elements above b*) + (elements of b* needed to reach T).
+//           same fixed-point masses, in digits of 8 bits from the highest key bit in
+//           which they differ: W = (elements above b*) + (elements of b* needed to reach T).
 //           Rows whose b* elements did not fit the buffer (or whose crossing lies in the
 //           tail, which only a near-tie allows) are refined by the whole block from
 //           the logits in global memory, filtered to b*.
@@ -36,7 +36,11 @@ typedef unsigned long long u64;
 constexpr int kXBins = 255;          // bins of width 1/16 covering x in [0, 255/16); 255 = tail
 constexpr float kBinsPerNat = 16.0f;
 constexpr int kCandCap = 6144;       // crossing-bin elements held in LDS (all 8 rows)
-constexpr int kKeepCap = 512;        // threshold buffer of keep-set candidates
+// Threshold buffer of keep-set candidates: 512 keys for pages of up to 64 slots (a unit
+// evicts at most one page), 1024 above, so that after a compaction down to the E
+// smallest keys at least one more round of 256 new keys fits before the next one (and
+// three blocks still share a CU's LDS).
+constexpr int keep_cap(int P) { return P <= 64 ? 512 : 1024; }
 
 enum { MODE_DONE = 0, MODE_LDS = 1, MODE_GLOBAL = 2 };
 
@@ -53,37 +57,13 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ u64 wave_exscan_u64(u64 v, int lane, u64* total) {
-  u64 x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const u64 y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  *total = __shfl(x, 63, 64);
+__device__ __forceinline__ u64 wave_exscan_u64(u64 v, u64* total) {
+  const u64 x = wave_incl_sum_u64(v);
+  *total = lane_u64(x, 63);
   return x - v;
 }
 
-__device__ __forceinline__ uint32_t wave_exscan_u32(uint32_t v, int lane) {
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  return x - v;
-}
-
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  return v;
-}
+__device__ __forceinline__ uint32_t wave_exscan_u32(uint32_t v) { return wave_incl_sum_u32(v) - v; }
 
 // Walk 256 bins (lane l owns 4 consecutive bins in walk order; DESC walks bin 255 first)
 // accumulating mass from (base_mass, base_cnt); return the first bin where the mass
@@ -106,8 +86,8 @@ __device__ __forceinline__ bool wave_find_crossing(const uint32_t* cnt, const u6
     lc += c4[q];
   }
   u64 tot = 0;
-  u64 acc = base_mass + wave_exscan_u64(ls, lane, &tot);
-  uint32_t ac = base_cnt + wave_exscan_u32(lc, lane);
+  u64 acc = base_mass + wave_exscan_u64(ls, &tot);
+  uint32_t ac = base_cnt + wave_exscan_u32(lc);
   int my = -1;
   u64 my_m = 0;
   uint32_t my_c = 0;
@@ -127,9 +107,9 @@ __device__ __forceinline__ bool wave_find_crossing(const uint32_t* cnt, const u6
   const u64 bal = __ballot(my >= 0);
   if (bal == 0) return false;
   const int f = __builtin_ctzll(bal);
-  *chosen = __shfl(my, f, 64);
-  *mass_before = __shfl(my_m, f, 64);
-  *cnt_before = __shfl(my_c, f, 64);
+  *chosen = (int)lane_u32((uint32_t)my, f);
+  *mass_before = lane_u64(my_m, f);
+  *cnt_before = lane_u32(my_c, f);
   return true;
 }
 
@@ -160,7 +140,12 @@ __device__ int wave_refine_lds(const float* src, int m, float M, u64 T, u64 acc_
   const int hb = 31 - __builtin_clz(kmin ^ kmax);     // highest differing bit
   uint32_t mask = hb >= 31 ? 0u : ~((2u << hb) - 1u);  // bits above hb: common to all
   uint32_t prefix = kmin & mask;
-  for (int shift = (hb / 8) * 8; shift >= 0; shift -= 8) {
+  // digits of up to 8 bits from the highest differing bit down
+  for (int top = hb + 1; top > 0;) {
+    const int w = min(8, top);
+    const int shift = top - w;
+    const uint32_t dmask = (1u << w) - 1u;
+    top = shift;
     for (int q = lane; q < 256; q += 64) {
       hcnt[q] = 0;
       hms[q] = 0;
@@ -170,7 +155,7 @@ __device__ int wave_refine_lds(const float* src, int m, float M, u64 T, u64 acc_
       const float v = src[c];
       const uint32_t key = ord_key(v);
       if ((key & mask) == prefix) {
-        const uint32_t bin = (key >> shift) & 255u;
+        const uint32_t bin = (key >> shift) & dmask;
         atomicAdd(&hcnt[bin], 1u);
         atomicAdd(&hms[bin], (u64)fixed_mass(v - M));
       }
@@ -184,7 +169,7 @@ __device__ int wave_refine_lds(const float* src, int m, float M, u64 T, u64 acc_
       acc_cnt = cb;
       prefix |= (uint32_t)chosen << shift;
     }
-    mask |= 255u << shift;
+    mask |= dmask << shift;
     wave_lds_sync();
   }
   return finish_w(prefix, M, T, acc_mass, acc_cnt, n);
@@ -218,7 +203,11 @@ __device__ int block_refine_global(const float* row, int n, int bstar, float M, 
   const int hb = 31 - __builtin_clz(kmin ^ kmax);
   uint32_t mask = hb >= 31 ? 0u : ~((2u << hb) - 1u);
   uint32_t prefix = kmin & mask;
-  for (int shift = (hb / 8) * 8; shift >= 0; shift -= 8) {
+  for (int top = hb + 1; top > 0;) {
+    const int w = min(8, top);
+    const int shift = top - w;
+    const uint32_t dmask = (1u << w) - 1u;
+    top = shift;
     hcnt[tid] = 0;
     hms[tid] = 0;
     __syncthreads();
@@ -226,7 +215,7 @@ __device__ int block_refine_global(const float* row, int n, int bstar, float M, 
       const float v = row[(int64_t)i * kDists];
       const uint32_t key = ord_key(v);
       if (x_bin(M - v) == bstar && (key & mask) == prefix) {
-        const uint32_t bin = (key >> shift) & 255u;
+        const uint32_t bin = (key >> shift) & dmask;
         atomicAdd(&hcnt[bin], 1u);
         atomicAdd(&hms[bin], (u64)fixed_mass(v - M));
       }
@@ -251,33 +240,41 @@ __device__ int block_refine_global(const float* row, int n, int bstar, float M, 
       acc_cnt = red[2];
       acc_mass = ((u64)red[4] << 32) | red[3];
     }
-    mask |= 255u << shift;
+    mask |= dmask << shift;
     __syncthreads();
   }
   return finish_w(prefix, M, T, acc_mass, acc_cnt, n);
 }
 
-__device__ void bitonic_sort_512(u64* a, int tid) {
-  for (int size = 2; size <= kKeepCap; size <<= 1) {
+// Ascending bitonic sort of CAP (a power of two, >= 512) keys by 256 threads.
+template <int CAP>
+__device__ void bitonic_sort(u64* a, int tid) {
+#pragma unroll
+  for (int size = 2; size <= CAP; size <<= 1) {
+#pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const int lo = 2 * tid - (tid & (stride - 1));
-      const int hi = lo + stride;
-      const bool asc = (lo & size) == 0;
-      const u64 x = a[lo], y = a[hi];
-      if ((x > y) == asc) {
-        a[lo] = y;
-        a[hi] = x;
+#pragma unroll
+      for (int t = tid; t < CAP / 2; t += 256) {
+        const int lo = 2 * t - (t & (stride - 1));
+        const int hi = lo + stride;
+        const bool asc = (lo & size) == 0;
+        const u64 x = a[lo], y = a[hi];
+        if ((x > y) == asc) {
+          a[lo] = y;
+          a[hi] = x;
+        }
       }
       __syncthreads();
     }
   }
 }
 
+template <int KCAP>
 __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
   const Geo& g = a.g;
   __shared__ u64 ms[kDists][256];          // read 1 bins; later refinement histograms
   __shared__ float cand[kCandCap];
-  __shared__ u64 kbuf[kKeepCap];
+  __shared__ u64 kbuf[KCAP];
   __shared__ float s_M[kDists], s_iz[kDists];
   __shared__ u64 s_T[kDists], s_above[kDists], s_Z[kDists];
   __shared__ uint32_t s_above_cnt[kDists], s_red[8];
@@ -302,6 +299,7 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
   }
   const int n = a.sp.n_tok[b];
   const int r = g.req_ids[b];
+  constexpr int kcap = KCAP;
   const int kk = g.n_alloc[r] * g.P;                  // slots a compaction keeps
   const int E = min(max(n - kk, 0), g.P);             // slots it evicts (fill <= P)
   const int nl = min(max(a.n_local, 0), min(kk, n));
@@ -375,7 +373,7 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) ls += ms[k][4 * lane + q];
     u64 Z = 0;
-    wave_exscan_u64(ls, lane, &Z);
+    wave_exscan_u64(ls, &Z);
     u64 T = 0;
     int mode = MODE_LDS, W = 0, chosen = kXBins;
     u64 mb = 0;
@@ -484,10 +482,10 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
       }
     }
     __syncthreads();
-    if (s_kcount > 256) {
-      for (int j = s_kcount + tid; j < kKeepCap; j += 256) kbuf[j] = ~0ull;
+    if (s_kcount > kcap - 256) {  // the next round might not fit: keep the E smallest
+      for (int j = s_kcount + tid; j < kcap; j += 256) kbuf[j] = ~0ull;
       __syncthreads();
-      bitonic_sort_512(kbuf, tid);
+      bitonic_sort<KCAP>(kbuf, tid);
       if (tid == 0) {
         s_kcount = E;
         s_ktau = kbuf[E - 1];
@@ -502,9 +500,9 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
   }
   if (tid < kDists && s_mode[tid] == MODE_LDS && s_fill[tid] > s_ub[tid]) s_mode[tid] = MODE_GLOBAL;
   if (E > 0) {
-    for (int j = s_kcount + tid; j < kKeepCap; j += 256) kbuf[j] = ~0ull;
+    for (int j = s_kcount + tid; j < kcap; j += 256) kbuf[j] = ~0ull;
     __syncthreads();
-    bitonic_sort_512(kbuf, tid);
+    bitonic_sort<KCAP>(kbuf, tid);
     // the E smallest keys are the evicted slots; store them in slot order
     if (tid < E) {
       const uint32_t s = (uint32_t)(kbuf[tid] & 0xffffffffu);
@@ -553,7 +551,10 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
 
 hipError_t launch_finish(const FinishArgs& a, hipStream_t st) {
   const int64_t units = (int64_t)a.g.n_req * a.g.L * a.g.Hkv;
-  hipLaunchKernelGGL(finish_kernel, dim3((unsigned)units), dim3(256), 0, st, a);
+  if (keep_cap(a.g.P) == 512)
+    hipLaunchKernelGGL(finish_kernel<512>, dim3((unsigned)units), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(finish_kernel<1024>, dim3((unsigned)units), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
