@@ -25,7 +25,7 @@ GP_NUM_COUNTERS = len(COUNTER_NAMES)
 EXPORTED = ("gp_abi_version", "gp_status_string", "gp_last_hip_error_string", "gp_update_summaries",
             "gp_scratch_bytes",
             "gp_boundary_scan", "gp_decide", "gp_decide_policy", "gp_compact", "gp_compact_prepare",
-            "gp_compact_move", "gp_append_kv")
+            "gp_compact_move", "gp_append_kv", "gp_decode_attention")
 # decision policies (gp_decide_policy)
 POLICIES = {"growpage": 0, "random": 1, "inverse": 2, "always_compact": 3}
 
@@ -98,6 +98,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gp_compact_move.restype = i32
     lib.gp_compact_move.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Pages), P, i32, P, P, sz,
                                     i64, P]
+    lib.gp_decode_attention.restype = i32
+    lib.gp_decode_attention.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Pages), P, i32, i64, i64, i64, P,
+                                        i32, P, P, i32, P, P, P]
     lib.gp_append_kv.restype = i32
     lib.gp_append_kv.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Pages), P, P, P, i32, P, P]
     _lib = lib
@@ -222,3 +225,11 @@ def append_kv(kv: KV, pages: Pages, k_new, v_new, req_ids, n_req, status_out=Non
     st = load().gp_append_kv(ctypes.byref(kv), ctypes.byref(pages), _ptr(k_new), _ptr(v_new),
                              _ptr(req_ids), int(n_req), _ptr(status_out), _stream(stream))
     _check(st, "gp_append_kv")
+
+
+def decode_attention(kv: KV, pages: Pages, q, q_dtype, q_strides, req_ids, n_req, rope_cos, rope_sin,
+                     rope_max_pos, pos, out, stream=None):
+    st = load().gp_decode_attention(ctypes.byref(kv), ctypes.byref(pages), _ptr(q), int(q_dtype),
+                                    *[int(x) for x in q_strides], _ptr(req_ids), int(n_req), _ptr(rope_cos),
+                                    _ptr(rope_sin), int(rope_max_pos), _ptr(pos), _ptr(out), _stream(stream))
+    _check(st, "gp_decode_attention")

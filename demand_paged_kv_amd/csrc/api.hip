@@ -240,4 +240,22 @@ gp_status gp_append_kv(const gp_kv* kv, const gp_pages* pages, const void* k_new
   return from_hip(launch_append(g, *pages, k_new, v_new, status_out, (hipStream_t)stream));
 }
 
+gp_status gp_decode_attention(const gp_kv* kv, const gp_pages* pages, const void* q, int32_t q_dtype,
+                              int64_t q_stride_req, int64_t q_stride_layer, int64_t q_stride_head,
+                              const int32_t* req_ids, int32_t n_req, const float* rope_cos,
+                              const float* rope_sin, int32_t rope_max_pos, const int32_t* pos,
+                              float* out, void* stream) {
+  if (gp_status s = check_kv(kv)) return s;
+  if (gp_status s = check_pages(pages, false)) return s;
+  if (n_req < 0 || n_req > pages->max_req) return GP_ERR_INVALID;
+  if (n_req == 0) return GP_OK;
+  if (!q || !req_ids || !out) return GP_ERR_INVALID;
+  if (q_dtype != GP_F32 && q_dtype != GP_BF16) return GP_ERR_INVALID;
+  if (rope_cos && (!rope_sin || !pos || rope_max_pos <= 0)) return GP_ERR_INVALID;
+  const Geo g = make_geo(kv, pages, req_ids, n_req);
+  return from_hip(launch_decode_attention(g, q, q_dtype, q_stride_req, q_stride_layer, q_stride_head,
+                                          rope_cos, rope_sin, rope_max_pos, pos, out,
+                                          (hipStream_t)stream));
+}
+
 }  // extern "C"

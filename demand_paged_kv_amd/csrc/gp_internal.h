@@ -150,4 +150,9 @@ hipError_t launch_compact_move(const Geo& g, const gp_pages& pg, const ScratchPt
 hipError_t launch_append(const Geo& g, const gp_pages& pg, const void* k_new, const void* v_new,
                          int32_t* status_out, hipStream_t st);
 
+hipError_t launch_decode_attention(const Geo& g, const void* q, int32_t q_dtype, int64_t sr, int64_t sl,
+                                   int64_t sh, const float* rope_cos, const float* rope_sin,
+                                   int32_t rope_max_pos, const int32_t* pos, float* out,
+                                   hipStream_t st);
+
 }  // namespace gp

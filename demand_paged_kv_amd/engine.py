@@ -152,6 +152,17 @@ class BoundaryEngine:
         B.append_kv(self.kv, self.pages, k_new, v_new, req_ids, int(req_ids.numel()), status_out,
                     stream)
 
+    def decode_attention(self, q: torch.Tensor, req_ids: torch.Tensor, out: torch.Tensor, stream=None):
+        """out[b][l][h] = attention of q[b][l][h] (pre-RoPE, rotated to st.pos) over the
+        request's retained slots; q [n][L][Hq][d] bf16/float32, out float32 contiguous."""
+        st = self.st
+        qd = B.GP_BF16 if q.dtype == torch.bfloat16 else B.GP_F32
+        max_pos = 0 if st.rope_cos is None else int(st.rope_cos.shape[0])
+        assert out.dtype == torch.float32 and out.is_contiguous()
+        B.decode_attention(self.kv, self.pages, q, qd, (q.stride(0), q.stride(1), q.stride(2)), req_ids,
+                           int(req_ids.numel()), st.rope_cos, st.rope_sin, max_pos,
+                           st.pos if st.rope_cos is not None else None, out, stream)
+
     def decode_step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                     req_ids: torch.Tensor, boundary_ids: Optional[torch.Tensor] = None,
                     stream=None) -> Optional[StepOutputs]:

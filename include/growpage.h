@@ -241,6 +241,21 @@ gp_status gp_append_kv(const gp_kv* kv, const gp_pages* pages, const void* k_new
                        const void* v_new, const int32_t* req_ids, int32_t n_req,
                        int32_t* status_out, void* stream);
 
+/* Decode attention over the paged cache -- the consumer of the pages the engine rewrites
+ * (GrowPage review, abstract and FAQ "How does GrowPage differ from Zipage?": the engine
+ * works inside PagedAttention serving).  For batch entry b (request slot r =
+ * req_ids[b]), layer l and query head h: out[b][l][h][:] = sum_i a_i v_i over the
+ * request's n = n_alloc[r]*P + fill[r] slots, a = softmax(qr . k_i / sqrt(d)), where qr
+ * is q[b][l][h] rotated to pos[r] (rotate-half pairs i, i + d/2, caller's table as in
+ * gp_boundary_scan; rope_cos == NULL: identity).  q: element strides like
+ * gp_update_summaries, bf16 or float32; out: [n_req][L][Hq][d] float32 (zeros for n ==
+ * 0).  Reads the pool only. */
+gp_status gp_decode_attention(const gp_kv* kv, const gp_pages* pages, const void* q, int32_t q_dtype,
+                              int64_t q_stride_req, int64_t q_stride_layer, int64_t q_stride_head,
+                              const int32_t* req_ids, int32_t n_req, const float* rope_cos,
+                              const float* rope_sin, int32_t rope_max_pos, const int32_t* pos,
+                              float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -448,6 +448,34 @@ def boundary_step(wl, sum_s: np.ndarray, sum_l: np.ndarray, params: dict) -> Ste
                       imps, e_req, table, A, fill, refcount, stack, top, k_new, v_new, cow, counters)
 
 
+# ----------------------------------------------------------------------------- decode attention
+def decode_attention(k_rows: np.ndarray, v_rows: np.ndarray, dtype: str, q: np.ndarray, q_dtype: str,
+                     cos_row, sin_row) -> np.ndarray:
+    """Attention of one request's decode queries over its retained slots, the reader of the
+    pages the engine rewrites [Abstract: the engine works inside PagedAttention serving].
+    Standard softmax attention in float64: each query head h of KV head g is rotated to
+    the request position (R4), scored against every stored key with scale 1/sqrt(d),
+    and the softmax weights average the stored values.  k_rows, v_rows [L][Hkv][n][d],
+    q [L][Hq][d]; returns [L][Hq][d] (zeros when n == 0)."""
+    L, Hkv, n, d = k_rows.shape
+    Hq = q.shape[1]
+    G = Hq // Hkv
+    qf = query_f32(q, q_dtype).astype(np.float64)
+    out = np.zeros((L, Hq, d))
+    if n == 0:
+        return out
+    for l in range(L):
+        for g in range(Hkv):
+            kf = widen(k_rows[l, g], dtype)
+            vf = widen(v_rows[l, g], dtype)
+            for j in range(G):
+                h = g * G + j
+                qt = rope_rotate(qf[l, h], cos_row, sin_row)
+                M, Z, a = softmax_stats(logits(qt[None, :], kf))
+                out[l, h] = a[0] @ vf
+    return out
+
+
 # ----------------------------------------------------------------------------- decode loop
 @dataclasses.dataclass
 class LoopState:

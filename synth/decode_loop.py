@@ -44,6 +44,7 @@ class DecodeSpec:
     k_focus: float = 1.0         # focus amplitude in new keys, in units of sqrt(d)
     hh_frac: float = 0.1         # fraction of prompt keys along the initial focus
     phase: tuple = (32, 256)     # focused / diffuse phase lengths in steps (uniform)
+    stagger: bool = False        # request r starts with r % P rows in its write page
     params: dict = dataclasses.field(default_factory=lambda: dict(SW.PARAMS_DEFAULT))
 
     @property
@@ -60,7 +61,7 @@ class DecodeSpec:
 
     @property
     def max_pos(self) -> int:
-        return self.prompt + self.steps
+        return self.prompt + self.P + self.steps
 
 
 def _rotate(u: torch.Tensor, c: torch.Tensor, s: torch.Tensor) -> torch.Tensor:
@@ -105,8 +106,15 @@ class DecodeLoopGen:
     def _randn(self, shape):
         return torch.randn(shape, generator=self.gen, device=self.device, dtype=torch.float32)
 
+    @property
+    def fill0(self) -> np.ndarray:
+        """Rows in each request's write page before the first decode step."""
+        sp = self.spec
+        return (np.arange(sp.B) % sp.P) if sp.stagger else np.zeros(sp.B, np.int64)
+
     def initial_state(self) -> DeviceState:
-        """Prompts in A0 = prompt/P shuffled allocation pages plus an empty write page."""
+        """Prompts in A0 = prompt/P shuffled allocation pages plus a write page holding
+        fill0 further prompt rows (none unless staggered)."""
         sp, dev = self.spec, self.device
         A0, P = sp.A0, sp.P
         table = np.full((sp.B, sp.max_pages), -1, np.int32)
@@ -119,34 +127,37 @@ class DecodeLoopGen:
         stack[: len(free)] = free
         k_pool = torch.zeros((sp.L, sp.num_pages, sp.Hkv, P, sp.d), dtype=torch.bfloat16, device=dev)
         v_pool = torch.zeros_like(k_pool)
-        pages = torch.from_numpy(table[:, :A0].astype(np.int64)).to(dev)          # [B][A0]
-        c, s = self.cos[: sp.prompt], self.sin[: sp.prompt]
+        npg = A0 + 1 if sp.stagger else A0                                         # pages holding prompt rows
+        pages = torch.from_numpy(table[:, :npg].astype(np.int64)).to(dev)          # [B][npg]
+        T = npg * P
+        c, s = self.cos[:T], self.sin[:T]
         scale = sp.k_focus * math.sqrt(sp.d)
         for l in range(sp.L):
-            k = self._randn((sp.B, sp.Hkv, sp.prompt, sp.d))
-            hh = (torch.rand((sp.B, sp.Hkv, sp.prompt), generator=self.gen, device=dev) < sp.hh_frac).float()
-            dirs = _rotate(self.focus[:, l, :, None, :], c, s)                       # [B][Hkv][prompt][d]
+            k = self._randn((sp.B, sp.Hkv, T, sp.d))
+            hh = (torch.rand((sp.B, sp.Hkv, T), generator=self.gen, device=dev) < sp.hh_frac).float()
+            dirs = _rotate(self.focus[:, l, :, None, :], c, s)                       # [B][Hkv][T][d]
             k += (scale * hh)[..., None] * dirs
-            v = self._randn((sp.B, sp.Hkv, sp.prompt, sp.d))
+            v = self._randn((sp.B, sp.Hkv, T, sp.d))
             for src, pool in ((k, k_pool), (v, v_pool)):
-                blk = src.to(torch.bfloat16).view(sp.B, sp.Hkv, A0, P, sp.d).permute(0, 2, 1, 3, 4)
+                blk = src.to(torch.bfloat16).view(sp.B, sp.Hkv, npg, P, sp.d).permute(0, 2, 1, 3, 4)
                 pool[l][pages] = blk
             del k, v, dirs, hh
         return DeviceState(
             L=sp.L, Hq=sp.Hq, Hkv=sp.Hkv, d=sp.d, P=P, num_pages=sp.num_pages, dtype=Bd.GP_BF16,
             k_pool=k_pool, v_pool=v_pool, page_table=torch.from_numpy(table).to(dev),
             n_alloc=torch.full((sp.B,), A0, dtype=torch.int32, device=dev),
-            fill=torch.zeros(sp.B, dtype=torch.int32, device=dev),
+            fill=torch.from_numpy(self.fill0.astype(np.int32)).to(dev),
             refcount=torch.from_numpy(refcount).to(dev), free_stack=torch.from_numpy(stack).to(dev),
             free_top=torch.tensor([len(free)], dtype=torch.int32, device=dev),
             sum_s=torch.zeros((sp.B, sp.L, sp.Hq, sp.d), dtype=torch.float32, device=dev),
             sum_l=torch.zeros((sp.B, sp.L, sp.Hq, sp.d), dtype=torch.float32, device=dev),
-            pos=torch.full((sp.B,), sp.prompt, dtype=torch.int32, device=dev),
+            pos=torch.from_numpy((sp.prompt + self.fill0).astype(np.int32)).to(dev),
             rope_cos=self.cos, rope_sin=self.sin)
 
     def step(self):
         """Inputs of the next decode step: q [B][L][Hq][d], k, v [B][L][Hkv][d] (bf16).
-        The step's token (and its query) sit at absolute position prompt + t."""
+        Request r's token (and query) of step t sit at absolute position
+        prompt + fill0[r] + t."""
         sp = self.spec
         t = self.t
         assert t < sp.steps
@@ -156,8 +167,8 @@ class DecodeLoopGen:
         a = self.amp[t][:, None, None, None]                                          # [B][1][1][1]
         qf = (a * (sp.q_focus * math.sqrt(sp.d))) * self.focus                         # [B][L][Hkv][d]
         q = self._randn((sp.B, sp.L, sp.Hq, sp.d)) + qf.repeat_interleave(G, dim=2)
-        p = sp.prompt + t
-        kd = _rotate(self.focus, self.cos[p], self.sin[p])
+        p = torch.from_numpy((sp.prompt + self.fill0 + t).astype(np.int64)).to(self.device)   # [B]
+        kd = _rotate(self.focus, self.cos[p][:, None, None, :], self.sin[p][:, None, None, :])
         k = self._randn((sp.B, sp.L, sp.Hkv, sp.d)) + (a * (sp.k_focus * math.sqrt(sp.d))) * kd
         v = self._randn((sp.B, sp.L, sp.Hkv, sp.d))
         self.t += 1

@@ -495,3 +495,45 @@ def test_boundary_step_follows_the_policy():
     u = np.array([0.1, 0.9, 0.5, 0.2, 0.7, 0.05], np.float32)
     rnd = O.boundary_step(wl, wl.sum_s, wl.sum_l, dict(wl.params, policy="random", rand_u=u, grow_prob=0.3))
     assert np.array_equal(rnd.decision, (u < np.float32(0.3)).astype(rnd.decision.dtype))
+
+
+# ----------------------------------------------------------------------------- decode attention
+def test_decode_attention_closed_forms():
+    """Equal scores average the values; one key far ahead returns its value; a shift of
+    every score (a query component along a direction all keys share) changes nothing."""
+    rng = np.random.default_rng(8)
+    n, d = 12, 16
+    v = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+    k0 = np.zeros((1, 1, n, d), np.float32)
+    q = rng.standard_normal((1, 2, d)).astype(np.float32)
+    out = O.decode_attention(k0, v, "f32", q, "f32", None, None)
+    assert np.allclose(out[0, 0], v[0, 0].mean(axis=0), atol=1e-12)
+    k1 = k0.copy()
+    k1[0, 0, 5, 0] = 1000.0
+    q1 = np.zeros((1, 2, d), np.float32)
+    q1[0, :, 0] = 1.0
+    out1 = O.decode_attention(k1, v, "f32", q1, "f32", None, None)
+    assert np.allclose(out1[0, 1], v[0, 0, 5], atol=1e-9)
+    # every key shares the component e_1 = 3; a query along e_1 adds the same score to all
+    k2 = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+    k2[..., 1] = 3.0
+    qa = rng.standard_normal((1, 2, d)).astype(np.float32)
+    qa[..., 1] = 0.0
+    qb = qa.copy()
+    qb[..., 1] = 5.0
+    assert np.allclose(O.decode_attention(k2, v, "f32", qa, "f32", None, None),
+                       O.decode_attention(k2, v, "f32", qb, "f32", None, None), atol=1e-12)
+    assert np.all(O.decode_attention(k2[:, :, :0], v[:, :, :0], "f32", qa, "f32", None, None) == 0)
+
+
+def test_decode_attention_is_a_convex_combination():
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal((2, 2, 30, 8)).astype(np.float32)
+    v = rng.standard_normal((2, 2, 30, 8)).astype(np.float32)
+    q = rng.standard_normal((2, 8, 8)).astype(np.float32) * 3
+    out = O.decode_attention(k, v, "f32", q, "f32", None, None)
+    for l in range(2):
+        for h in range(8):
+            g = h // 4
+            assert np.all(out[l, h] <= v[l, g].max(axis=0) + 1e-12)
+            assert np.all(out[l, h] >= v[l, g].min(axis=0) - 1e-12)
