@@ -98,9 +98,9 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
 }
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const uint32_t lo = dpp_u32<CTRL, ROW_MASK>(0u, (uint32_t)v);
-  const uint32_t hi = dpp_u32<CTRL, ROW_MASK>(0u, (uint32_t)(v >> 32));
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v, uint64_t old = 0) {
+  const uint32_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)old, (uint32_t)v);
+  const uint32_t hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(old >> 32), (uint32_t)(v >> 32));
   return ((uint64_t)hi << 32) | lo;
 }
 
@@ -149,6 +149,26 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   x = max(x, dpp_u32<kDppRowBcast15, 0xA>(0u, x));
   x = max(x, dpp_u32<kDppRowBcast31, 0xC>(0u, x));
   return lane_u32(x, 63);
+}
+
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t x) {
+  constexpr uint64_t I = ~0ull;
+  x = min(x, dpp_u64<kDppRowShr1, 0xF>(x, I));
+  x = min(x, dpp_u64<kDppRowShr2, 0xF>(x, I));
+  x = min(x, dpp_u64<kDppRowShr4, 0xF>(x, I));
+  x = min(x, dpp_u64<kDppRowShr8, 0xF>(x, I));
+  x = min(x, dpp_u64<kDppRowBcast15, 0xA>(x, I));
+  x = min(x, dpp_u64<kDppRowBcast31, 0xC>(x, I));
+  return lane_u64(x, 63);
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+  x = max(x, dpp_u64<kDppRowShr1, 0xF>(x));
+  x = max(x, dpp_u64<kDppRowShr2, 0xF>(x));
+  x = max(x, dpp_u64<kDppRowShr4, 0xF>(x));
+  x = max(x, dpp_u64<kDppRowShr8, 0xF>(x));
+  x = max(x, dpp_u64<kDppRowBcast15, 0xA>(x));
+  x = max(x, dpp_u64<kDppRowBcast31, 0xC>(x));
+  return lane_u64(x, 63);
 }
 
 __device__ __forceinline__ int wave_sum_int(int v) {

@@ -17,7 +17,8 @@
 //           element of bin b carries at least the mass of x = (b+1)/16); in the same
 //           pass the slot importance max_k exp(l_k - M_k) / Z_k feeds a threshold
 //           buffer that keeps the n - k least important candidate slots (ties: older
-//           slot first) -- the slots a compaction evicts.
+//           slot first) -- the slots a compaction evicts; whenever the buffer fills, a
+//           radix select keeps its n - k smallest keys and lowers the threshold.
 //   refine  per row, an exact radix select over the b* elements only, weighted by the
 //           same fixed-point masses, in digits of 8 bits from the highest key bit in
 //           which they differ: W = (elements above b*) + (elements of b* needed to reach T).
@@ -35,7 +36,9 @@ typedef unsigned long long u64;
 
 constexpr int kXBins = 255;          // bins of width 1/16 covering x in [0, 255/16); 255 = tail
 constexpr float kBinsPerNat = 16.0f;
-constexpr int kCandCap = 6144;       // crossing-bin elements held in LDS (all 8 rows)
+// Crossing-bin elements held in LDS (all 8 rows): sized with the keep buffer so that a
+// block stays within 40 KB of LDS and four blocks (16 waves) share a CU.
+constexpr int cand_cap(int kcap) { return kcap == 512 ? 4864 : 3840; }
 // Threshold buffer of keep-set candidates: 512 keys for pages of up to 64 slots (a unit
 // evicts at most one page), 1024 above, so that after a compaction down to the E
 // smallest keys at least one more round of 256 new keys fits before the next one (and
@@ -246,31 +249,100 @@ __device__ int block_refine_global(const float* row, int n, int bstar, float M, 
   return finish_w(prefix, M, T, acc_mass, acc_cnt, n);
 }
 
-// Ascending bitonic sort of CAP (a power of two, >= 512) keys by 256 threads.
-template <int CAP>
-__device__ void bitonic_sort(u64* a, int tid) {
+// Bits of a 64-bit key above bit position top - 1 (top in 0..64).
+__device__ __forceinline__ u64 mask_above(int top) { return top >= 64 ? 0ull : ~((1ull << top) - 1ull); }
+
+// The kth smallest (1-based) of cnt distinct keys in LDS, by a block-wide radix select:
+// 8-bit digits from the highest bit in which the keys differ, each pass histogramming
+// the keys that match the digits chosen so far; it stops as soon as the chosen digit's
+// bucket holds one key.  hist: 256 LDS counters; sx: 8 LDS scratch words.
+// Block-uniform control flow.
+__device__ u64 block_kth_smallest(const u64* keys, int cnt, int kth, uint32_t* hist, u64* sx, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  u64 kmin = ~0ull, kmax = 0;
+  for (int i = tid; i < cnt; i += 256) {
+    kmin = min(kmin, keys[i]);
+    kmax = max(kmax, keys[i]);
+  }
+  kmin = wave_min_u64(kmin);
+  kmax = wave_max_u64(kmax);
+  if (lane == 0) {
+    sx[wave] = kmin;
+    sx[4 + wave] = kmax;
+  }
+  __syncthreads();
+  kmin = min(min(sx[0], sx[1]), min(sx[2], sx[3]));
+  kmax = max(max(sx[4], sx[5]), max(sx[6], sx[7]));
+  __syncthreads();
+  if (kmin == kmax) return kmin;
+  const int hb = 63 - __builtin_clzll(kmin ^ kmax);
+  u64 prefix = kmin & mask_above(hb + 1);
+  int need = kth;
+  for (int top = hb + 1; top > 0;) {
+    const int w = min(8, top);
+    const int shift = top - w;
+    const uint32_t dmask = (1u << w) - 1u;
+    const u64 hmask = mask_above(top);
+    hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < cnt; i += 256) {
+      const u64 key = keys[i];
+      if (((key ^ prefix) & hmask) == 0) atomicAdd(&hist[(uint32_t)(key >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {  // ascending walk: the first digit whose cumulative count reaches need
+      uint32_t c4[4], ls = 0;
 #pragma unroll
-  for (int size = 2; size <= CAP; size <<= 1) {
+      for (int q = 0; q < 4; ++q) {
+        c4[q] = hist[4 * lane + q];
+        ls += c4[q];
+      }
+      uint32_t acc = wave_incl_sum_u32(ls) - ls;
+      int my = -1;
+      uint32_t before = 0, inbin = 0;
 #pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-#pragma unroll
-      for (int t = tid; t < CAP / 2; t += 256) {
-        const int lo = 2 * t - (t & (stride - 1));
-        const int hi = lo + stride;
-        const bool asc = (lo & size) == 0;
-        const u64 x = a[lo], y = a[hi];
-        if ((x > y) == asc) {
-          a[lo] = y;
-          a[hi] = x;
+      for (int q = 0; q < 4; ++q) {
+        if (my < 0) {
+          if (acc + c4[q] >= (uint32_t)need) {
+            my = 4 * lane + q;
+            before = acc;
+            inbin = c4[q];
+          } else {
+            acc += c4[q];
+          }
         }
       }
+      const u64 bal = __ballot(my >= 0);
+      const int f = bal ? __builtin_ctzll(bal) : 0;
+      if (lane == 0) {
+        sx[0] = lane_u32((uint32_t)my, f);
+        sx[1] = lane_u32(before, f);
+        sx[2] = lane_u32(inbin, f);
+      }
+    }
+    __syncthreads();
+    const u64 d = sx[0];
+    need -= (int)sx[1];
+    const u64 inbin = sx[2];
+    __syncthreads();
+    prefix |= d << shift;
+    top = shift;
+    if (inbin == 1 && top > 0) {  // one key left in the bucket: it is the answer
+      const u64 m2 = mask_above(top);
+      for (int i = tid; i < cnt; i += 256)
+        if (((keys[i] ^ prefix) & m2) == 0) sx[3] = keys[i];
       __syncthreads();
+      prefix = sx[3];
+      __syncthreads();
+      break;
     }
   }
+  return prefix;
 }
 
 template <int KCAP>
-__global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void finish_kernel(FinishArgs a) {
+  constexpr int kCandCap = cand_cap(KCAP);
   const Geo& g = a.g;
   __shared__ u64 ms[kDists][256];          // read 1 bins; later refinement histograms
   __shared__ float cand[kCandCap];
@@ -279,8 +351,12 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
   __shared__ u64 s_T[kDists], s_above[kDists], s_Z[kDists];
   __shared__ uint32_t s_above_cnt[kDists], s_red[8];
   __shared__ int s_mode[kDists], s_bin[kDists], s_off[kDists], s_fill[kDists], s_ub[kDists], s_W[kDists];
-  __shared__ int s_kcount;
-  __shared__ u64 s_ktau;
+  __shared__ int s_kcount, s_c2;
+  __shared__ u64 s_ktau, s_x[8];
+  // keep-set selection works in the read-1 bins, free between the crossing search and
+  // the refinement: 256 digit counters, then up to 256 selected keys
+  uint32_t* sel_hist = reinterpret_cast<uint32_t*>(&ms[0][0]);
+  u64* sel_tmp = &ms[1][0];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -482,13 +558,18 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
       }
     }
     __syncthreads();
-    if (s_kcount > kcap - 256) {  // the next round might not fit: keep the E smallest
-      for (int j = s_kcount + tid; j < kcap; j += 256) kbuf[j] = ~0ull;
+    const int cnt = s_kcount;
+    if (cnt > kcap - 256) {  // the next round might not fit: keep the E smallest
+      const u64 K = block_kth_smallest(kbuf, cnt, E, sel_hist, s_x, tid);
+      if (tid == 0) s_c2 = 0;
       __syncthreads();
-      bitonic_sort<KCAP>(kbuf, tid);
+      for (int j = tid; j < cnt; j += 256)
+        if (kbuf[j] <= K) sel_tmp[atomicAdd(&s_c2, 1)] = kbuf[j];
+      __syncthreads();
+      for (int j = tid; j < E; j += 256) kbuf[j] = sel_tmp[j];
       if (tid == 0) {
         s_kcount = E;
-        s_ktau = kbuf[E - 1];
+        s_ktau = K;
       }
       __syncthreads();
     }
@@ -500,14 +581,19 @@ __global__ __launch_bounds__(256) void finish_kernel(FinishArgs a) {
   }
   if (tid < kDists && s_mode[tid] == MODE_LDS && s_fill[tid] > s_ub[tid]) s_mode[tid] = MODE_GLOBAL;
   if (E > 0) {
-    for (int j = s_kcount + tid; j < kcap; j += 256) kbuf[j] = ~0ull;
-    __syncthreads();
-    bitonic_sort<KCAP>(kbuf, tid);
     // the E smallest keys are the evicted slots; store them in slot order
+    const int cnt = s_kcount;
+    const u64 K = block_kth_smallest(kbuf, cnt, E, sel_hist, s_x, tid);
+    uint32_t* sel = reinterpret_cast<uint32_t*>(sel_tmp);
+    if (tid == 0) s_c2 = 0;
+    __syncthreads();
+    for (int j = tid; j < cnt; j += 256)
+      if (kbuf[j] <= K) sel[atomicAdd(&s_c2, 1)] = (uint32_t)(kbuf[j] & 0xffffffffu);
+    __syncthreads();
     if (tid < E) {
-      const uint32_t s = (uint32_t)(kbuf[tid] & 0xffffffffu);
+      const uint32_t s = sel[tid];
       int rk = 0;
-      for (int j = 0; j < E; ++j) rk += (uint32_t)(kbuf[j] & 0xffffffffu) < s ? 1 : 0;
+      for (int j = 0; j < E; ++j) rk += sel[j] < s ? 1 : 0;
       a.sp.ev[u * g.P + rk] = (int)s;
       if (rk == 0) a.sp.e_unit[u] = (int)s;
     }
