@@ -263,19 +263,7 @@ __global__ __launch_bounds__(256) void gather_kernel(CompactArgs a) {
   const int units = g.n_req * g.L * g.Hkv;
   const int which = blockIdx.x >= units ? 1 : 0;
   int b, l, kvh;
-#ifdef GP_GATHER_LAYER_MAJOR
-  {
-    const int blk = blockIdx.x - which * units;
-    const int per_layer = g.n_req * g.Hkv;
-    l = blk / per_layer;
-    const int rem = blk - l * per_layer;
-    const int rank = rem / g.Hkv;
-    kvh = rem - rank * g.Hkv;
-    b = a.sp.order[rank];
-  }
-#else
   unit_of_block(g, a.sp, blockIdx.x - which * units, b, l, kvh);
-#endif
   const int32_t* rq = a.sp.req + (int64_t)b * RQ_N;
   if (rq[RQ_STATE] != ST_GO) return;
   const int r = g.req_ids[b];

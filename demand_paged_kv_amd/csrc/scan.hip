@@ -138,19 +138,11 @@ __global__ __launch_bounds__(64) void logit_kernel(ScanArgs a) {
   const int tl = lane >> 4;      // token of the step
   const int j = lane & 15;       // element slice
   const int js = lane & 7;       // summary this lane ends a step with
-#ifdef GP_SCAN_LAYER_MAJOR
-  const int per_layer = g.n_req * g.Hkv;
-  const int l = blockIdx.x / per_layer;
-  const int rem = blockIdx.x - l * per_layer;
-  const int rank = rem / g.Hkv;
-  const int kvh = rem - rank * g.Hkv;
-#else
   const int upr = g.L * g.Hkv;
   const int rank = blockIdx.x / upr;
   const int rem = blockIdx.x - rank * upr;
   const int l = rem / g.Hkv;
   const int kvh = rem - l * g.Hkv;
-#endif
   const int b = a.sp.order[rank];
   if (a.sp.flags[b]) return;
   const int n = a.sp.n_tok[b];
@@ -194,13 +186,29 @@ __global__ __launch_bounds__(64) void logit_kernel(ScanArgs a) {
   float m = -INFINITY;
 
   // Full batches of U steps, loads of the next batch issued before this one is reduced.
-  // Page index and in-page offset are wave-uniform, so page ids come in by scalar loads.
+  // Page index and in-page offset are wave-uniform, so page ids come in by scalar loads,
+  // fetched one batch ahead of the row loads that use them (indexes clamped to the
+  // request's pages, so the look-ahead past the last batch stays in bounds).
   const int nfull = (n / (TS * U)) * (TS * U);
+  const int npages = (n + g.P - 1) / g.P;
   int pj = 0, sub = 0;  // page index and in-page offset of the next step to load
-  auto load_batch = [&](Chunk<BF16, D>(&c)[U]) {
+  int fq = 0, fs = 0;   // the same for the next page-id fetch
+  int pid[U];
+  auto fetch_pids = [&]() {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const char* row = kb + (int64_t)pt[pj] * page_bytes + (int64_t)sub * tok_bytes;
+      pid[u] = pt[min(fq, npages - 1)];
+      fs += TS;
+      if (fs == g.P) {
+        fs = 0;
+        ++fq;
+      }
+    }
+  };
+  auto load_batch = [&](Chunk<BF16, D>(&c)[U], const int (&ids)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const char* row = kb + (int64_t)ids[u] * page_bytes + (int64_t)sub * tok_bytes;
       load_chunk<BF16, D>(c[u], row, j);
       sub += TS;
       if (sub == g.P) {
@@ -210,9 +218,22 @@ __global__ __launch_bounds__(64) void logit_kernel(ScanArgs a) {
     }
   };
   Chunk<BF16, D> cur[U], nxt[U];
-  if (nfull > 0) load_batch(cur);
+  if (nfull > 0) {
+    fetch_pids();
+    int ids[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ids[u] = pid[u];
+    load_batch(cur, ids);
+    fetch_pids();
+  }
   for (int t0 = 0; t0 < nfull; t0 += TS * U) {
-    if (t0 + TS * U < nfull) load_batch(nxt);
+    if (t0 + TS * U < nfull) {
+      int ids[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) ids[u] = pid[u];
+      load_batch(nxt, ids);
+      fetch_pids();
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float x = step_scores<BF16, D>(cur[u], qr);

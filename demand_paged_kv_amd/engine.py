@@ -39,8 +39,11 @@ class DeviceState:
     rope_sin: Optional[torch.Tensor] = None
 
     def kv(self) -> B.KV:
-        return B.make_kv(self.k_pool, self.v_pool, self.L, self.Hq, self.Hkv, self.d, self.P,
-                         self.num_pages, self.dtype)
+        """The pools as [L][num_pages][Hkv][P][d] views (any strides, d contiguous)."""
+        k, v = self.k_pool, self.v_pool
+        assert k.shape == v.shape and k.stride() == v.stride() and k.stride(4) == 1
+        return B.make_kv(k, v, self.L, self.Hq, self.Hkv, self.d, self.P, self.num_pages, self.dtype,
+                         strides=k.stride()[:4])
 
     def pages(self) -> B.Pages:
         return B.make_pages(self.page_table, self.n_alloc, self.fill, self.refcount,

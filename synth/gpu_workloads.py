@@ -49,10 +49,22 @@ def _rotate(u: torch.Tensor, c: torch.Tensor, s: torch.Tensor) -> torch.Tensor:
     return torch.cat([x1 * c - x2 * s, x2 * c + x1 * s], dim=-1)
 
 
+def pool_pair(L, num_pages, Hkv, P, d, layout, device):
+    """K and V pools as [L][num_pages][Hkv][P][d] views: "layer_major" stores them in that
+    order; "page_major" stores [num_pages][L][Hkv][P][d] (all layers of a page together)."""
+    if layout == "layer_major":
+        k = torch.empty((L, num_pages, Hkv, P, d), dtype=torch.bfloat16, device=device)
+        return k, torch.empty_like(k)
+    assert layout == "page_major", layout
+    k = torch.empty((num_pages, L, Hkv, P, d), dtype=torch.bfloat16, device=device).permute(1, 0, 2, 3, 4)
+    v = torch.empty((num_pages, L, Hkv, P, d), dtype=torch.bfloat16, device=device).permute(1, 0, 2, 3, 4)
+    return k, v
+
+
 def boundary_sweep(seed: int = 3000, B: int = 64, L: int = 32, Hq: int = 32, Hkv: int = 8, d: int = 128,
                    P: int = 16, num_pages: int = 24576, ctx=(512, 16384), grow_frac: float = 0.3,
                    s_zipf: float = 1.1, params: dict | None = None, device="cuda",
-                   name: str = "boundary_sweep") -> GpuWorkload:
+                   name: str = "boundary_sweep", layout: str = "layer_major") -> GpuWorkload:
     rng = np.random.default_rng(seed)
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
@@ -89,8 +101,7 @@ def boundary_sweep(seed: int = 3000, B: int = 64, L: int = 32, Hq: int = 32, Hkv
     sum_s = (bs[..., None] * u + 0.1 * torch.randn((B, L, Hq, d), generator=gen, device=device, dtype=torch.float64)).float()
     sum_l = (bl[..., None] * u + 0.1 * torch.randn((B, L, Hq, d), generator=gen, device=device, dtype=torch.float64)).float()
 
-    k_pool = torch.empty((L, num_pages, Hkv, P, d), dtype=torch.bfloat16, device=device)
-    v_pool = torch.empty_like(k_pool)
+    k_pool, v_pool = pool_pair(L, num_pages, Hkv, P, d, layout, device)
     for l in range(L):           # V and unused K pages: N(0, 1)
         k_pool[l].normal_(generator=gen)
         v_pool[l].normal_(generator=gen)
