@@ -546,9 +546,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void f
         const float xv = M[k] - v;
         const int bin = x_bin(xv);
         above[k] += bin < binstar[k] ? 1u : 0u;
-        if (mode[k] == MODE_LDS && bin == binstar[k]) {
+        if (bin == binstar[k] && mode[k] != MODE_DONE) {  // counted for every row, kept for LDS rows
           const int p = atomicAdd(&s_fill[k], 1);
-          if (p < bub[k]) cand[boff[k] + p] = v;  // a count beyond the bound sends the row to the block path
+          if (mode[k] == MODE_LDS && p < bub[k]) cand[boff[k] + p] = v;  // beyond the bound: block path
         }
         imp = fmaxf(imp, exp2f(-xv * kLog2e) * iz[k]);  // keeps tiny results (denormals) ordered
       }
@@ -614,11 +614,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void f
     }
   }
   __syncthreads();
+  // Rows refined by the block: their crossing-bin elements are collected into the (now
+  // free) LDS candidate buffer by one filtered pass when they fit, and refined there;
+  // larger bins are refined in global memory.
   for (int k = 0; k < kDists; ++k) {
     if (s_mode[k] != MODE_GLOBAL) continue;  // block-uniform
-    const int Wr = block_refine_global(x + k, n, s_bin[k], M[k], s_T[k], s_above[k], s_above_cnt[k],
-                                       reinterpret_cast<uint32_t*>(&ms[0][0]), &ms[2][0], s_red, tid);
-    if (tid == 0) s_W[k] = Wr;
+    const float Mk = s_M[k];
+    if (s_fill[k] <= kCandCap) {
+      if (tid == 0) s_c2 = 0;
+      __syncthreads();
+      const int bk = s_bin[k];
+      for (int i = tid; i < n; i += 256) {
+        const float v = x[(int64_t)i * kDists + k];
+        if (x_bin(Mk - v) == bk) cand[atomicAdd(&s_c2, 1)] = v;
+      }
+      __syncthreads();
+      if (wave == 0) {
+        const int Wr = wave_refine_lds(cand, s_c2, Mk, s_T[k], s_above[k], s_above_cnt[k], hcnt, hms, lane, n);
+        if (lane == 0) s_W[k] = Wr;
+      }
+    } else {
+      const int Wr = block_refine_global(x + k, n, s_bin[k], Mk, s_T[k], s_above[k], s_above_cnt[k],
+                                         reinterpret_cast<uint32_t*>(&ms[0][0]), &ms[2][0], s_red, tid);
+      if (tid == 0) s_W[k] = Wr;
+    }
     __syncthreads();
   }
   if (tid < kDists) {
