@@ -8,12 +8,13 @@
 //                  the scratch, and a longest-first order of the entries.
 //   logit_kernel   one wave per (entry, layer, KV head) "unit", launched longest-first.
 //                  The wave streams the unit's K rows through the page table once;
-//                  8 lanes share a token row (each holds 2 x D/16 elements), every lane
-//                  keeps the matching slices of all 8 rotated summaries (4 query heads x
-//                  2 timescales) in registers, and a 3-step DPP transpose-reduce leaves
-//                  lane j with the logit of summary j for its token.  Logits go to the
-//                  scratch ([unit][n][8] float32: one wave step writes 256 contiguous
-//                  bytes), the running max to the statistics.
+//                  16 lanes share a token row (each holds D/16 contiguous elements), every
+//                  lane keeps the matching slices of all 8 rotated summaries (4 query heads
+//                  x 2 timescales) in registers, and a DPP transpose-reduce (3 steps within
+//                  each 8-lane half, one across the halves) leaves lane j with the logit of
+//                  summary j mod 8 for its token.  Logits go to the scratch ([unit][n][8]
+//                  float32: one wave step writes 128 contiguous bytes), the running max to
+//                  the statistics.
 //   finish_kernel  one block per unit: exact Top-p working sets of the 8 logit rows and
 //                  the unit's keep-set, from two reads of the logits.
 #include "device_util.h"
