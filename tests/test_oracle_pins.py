@@ -179,6 +179,15 @@ def test_working_set_brute_force_small():
             assert W == best
 
 
+def test_working_set_mass_exactly_p_counts():
+    """R1 asks for the smallest set whose mass reaches p (>=, not >): with dyadic masses
+    every partial sum is exact, so a prefix summing to exactly p ends the set there."""
+    a = np.array([0.125, 0.5, 0.125, 0.25])
+    assert O.working_set(a, 0.75)[0] == 2
+    assert O.working_set(a, 0.5)[0] == 1
+    assert O.working_set(a, 0.875)[0] == 3
+
+
 def test_working_set_limits_and_monotone():
     rng = np.random.default_rng(9)
     a = rng.exponential(size=300)
@@ -189,6 +198,19 @@ def test_working_set_limits_and_monotone():
     ws = [O.working_set(a, p)[0] for p in np.linspace(0.01, 0.999, 60)]
     assert all(x <= y for x, y in zip(ws, ws[1:]))
     assert O.working_set(np.zeros(0), 0.9) == (0, 0, 0)
+
+
+def test_scan_query_heads_share_their_group_kv_head():
+    """Grouped-query attention: query head h reads KV head h // G.  KV head 0 holds equal
+    keys (uniform weights, W = ceil(p n)), KV head 1 one dominant key (W = 1), so the
+    first G query heads see ceil(p n) and the rest 1."""
+    L, Hkv, G, n, d, p = 1, 2, 3, 40, 8, 0.9
+    k = np.zeros((L, Hkv, n, d), np.float32)
+    k[0, 1, 7, 0] = 1000.0
+    summ = np.zeros((L, Hkv * G, d), np.float32)
+    summ[..., 0] = 1.0
+    W, lo, hi, M, Z, _ = O.scan_request(k, "f32", summ, summ, None, None, p)
+    assert (W[0, :G] == 36).all() and (W[0, G:] == 1).all()
 
 
 # ----------------------------------------------------------------------------- decision (R2)
@@ -537,3 +559,41 @@ def test_decode_attention_is_a_convex_combination():
             g = h // 4
             assert np.all(out[l, h] <= v[l, g].max(axis=0) + 1e-12)
             assert np.all(out[l, h] >= v[l, g].min(axis=0) - 1e-12)
+
+
+def test_decode_attention_two_keys_closed_form():
+    """Two keys whose scores differ by a/sqrt(d): the weights are the logistic of that
+    difference, so the output is (e^x v_1 + v_2) / (e^x + 1) with x = a / sqrt(d)."""
+    d, a = 16, 3.0
+    k = np.zeros((1, 1, 2, d), np.float32)
+    k[0, 0, 0, 0] = a
+    v = np.random.default_rng(10).standard_normal((1, 1, 2, d)).astype(np.float32)
+    q = np.zeros((1, 4, d), np.float32)
+    q[0, :, 0] = 1.0
+    out = O.decode_attention(k, v, "f32", q, "f32", None, None)
+    x = a / math.sqrt(d)
+    want = (math.exp(x) * v[0, 0, 0].astype(np.float64) + v[0, 0, 1]) / (math.exp(x) + 1.0)
+    assert np.allclose(out[0, 3], want, atol=1e-12)
+
+
+def test_decode_attention_rotates_the_query_like_the_keys():
+    """A key stored rotated to position t scores like an unrotated key when the query is
+    rotated to the same position (a rotation preserves dot products), so against a
+    second key of score 0 the weights are the logistic of |u|^2 / sqrt(d)."""
+    d, t = 16, 37
+    cos, sin = SW.rope_tables(64, d)
+    u = np.random.default_rng(11).standard_normal(d)
+    u /= np.linalg.norm(u)
+    u *= 2.0
+    h = d // 2
+    kr = np.concatenate([u[:h] * cos[t] - u[h:] * sin[t], u[h:] * cos[t] + u[:h] * sin[t]])
+    k = np.zeros((1, 1, 2, d), np.float64)
+    k[0, 0, 0] = kr
+    v = np.random.default_rng(12).standard_normal((1, 1, 2, d))
+    q = np.tile(u, (1, 4, 1))
+    out = O.decode_attention(k.astype(np.float32), v.astype(np.float32), "f32", q.astype(np.float32), "f32",
+                             cos[t], sin[t])
+    x = float(np.dot(u.astype(np.float32).astype(np.float64), u.astype(np.float32).astype(np.float64))) / math.sqrt(d)
+    v32 = v.astype(np.float32).astype(np.float64)
+    want = (math.exp(x) * v32[0, 0, 0] + v32[0, 0, 1]) / (math.exp(x) + 1.0)
+    assert np.allclose(out[0, 0], want, atol=1e-5)
