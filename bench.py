@@ -177,7 +177,7 @@ def main():
         "compact_move": dict(bytes=move_bytes, ms=mean_ms["compact_move"]),
     }
     dom = max(per_kernel, key=lambda k: per_kernel[k]["ms"])
-    kname = {"scan": "gp_boundary_scan (plan_kernel + logit_kernel + finish_kernel)",
+    kname = {"scan": "gp_boundary_scan (plan_kernel + fused_scan_kernel)",
              "compact_move": "gather_kernel (gp_compact_move)"}[dom]
     achieved = per_kernel[dom]["bytes"] / (per_kernel[dom]["ms"] / 1e3) / 1e9
     traffic = None

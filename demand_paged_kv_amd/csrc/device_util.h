@@ -82,6 +82,14 @@ __device__ __forceinline__ int block_exscan_1024(int v, int* tmp, int* total) {
   return base + x - v;
 }
 
+// Order the LDS accesses of one wave without a block barrier.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---- wave64 prefix scans and reductions on DPP lane moves (no LDS traffic).  Each
 // step moves a value within rows of 16 lanes (row_shr) or from the last lane of one row
 // to the following rows (row_bcast15 / row_bcast31); lanes a step does not write keep

@@ -4,7 +4,8 @@
 // FAQ "Is GrowPage's code available?": local retention quota.)
 //
 // One 256-thread block per (entry, layer, KV head) unit, two reads of the unit's logits
-// ([n][8] float32, token-major, written by the logit kernel with each row's max M):
+// ([n][8] float32, token-major, with each row's max M), which either the same block has
+// just computed (fused_scan_kernel, at the end of this file) or logit_kernel wrote:
 //
 //   read 1  x = M - l >= 0 for every element of the 8 rows.  Each element adds its
 //           softmax mass exp(-x) (2^-40 fixed point, one 64-bit LDS atomic) to one of
@@ -28,6 +29,7 @@
 // All decisions are exact for the float32 logits the scan produced.
 #include "device_util.h"
 #include "gp_internal.h"
+#include "logit_mfma.h"
 
 namespace gp {
 namespace {
@@ -50,14 +52,6 @@ enum { MODE_DONE = 0, MODE_LDS = 1, MODE_GLOBAL = 2 };
 __device__ __forceinline__ int x_bin(float xv) {
   const float f = xv * kBinsPerNat;
   return f < (float)kXBins ? (int)f : kXBins;
-}
-
-// Order the LDS accesses of one wave without a block barrier.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __device__ __forceinline__ u64 wave_exscan_u64(u64 v, u64* total) {
@@ -340,13 +334,24 @@ __device__ u64 block_kth_smallest(const u64* keys, int cnt, int kth, uint32_t* h
   return prefix;
 }
 
+// Working sets and keep-set of unit (entry at rank `rank`, layer l, KV head kvh), by one
+// 256-thread block.
+// The block's large LDS arrays, laid out back to back in one buffer (the fused kernel
+// uses the same bytes to stage logits before the selection starts).
 template <int KCAP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void finish_kernel(FinishArgs a) {
+struct FinishLds {
+  u64 ms[kDists][256];          // read 1 bins; later refinement histograms
+  float cand[cand_cap(KCAP)];   // crossing-bin elements
+  u64 kbuf[KCAP];               // keep-set threshold buffer
+};
+
+template <int KCAP>
+__device__ __forceinline__ void finish_unit(const FinishArgs& a, int rank, int l, int kvh, FinishLds<KCAP>& lds) {
   constexpr int kCandCap = cand_cap(KCAP);
   const Geo& g = a.g;
-  __shared__ u64 ms[kDists][256];          // read 1 bins; later refinement histograms
-  __shared__ float cand[kCandCap];
-  __shared__ u64 kbuf[KCAP];
+  u64 (*ms)[256] = lds.ms;
+  float* cand = lds.cand;
+  u64* kbuf = lds.kbuf;
   __shared__ float s_M[kDists], s_iz[kDists];
   __shared__ u64 s_T[kDists], s_above[kDists], s_Z[kDists];
   __shared__ uint32_t s_above_cnt[kDists], s_red[8];
@@ -361,11 +366,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void f
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int upr = g.L * g.Hkv;
-  const int rank = blockIdx.x / upr;
-  const int rem = blockIdx.x - rank * upr;
-  const int l = rem / g.Hkv;
-  const int kvh = rem - l * g.Hkv;
   const int b = a.sp.order[rank];
   const int64_t u = ((int64_t)b * g.L + l) * g.Hkv + kvh;
   auto widx = [&](int k) { return (((int64_t)b * g.L + l) * g.Hq + kvh * kGroup + (k >> 1)) * 2 + (k & 1); };
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void f
   const int E = min(max(n - kk, 0), g.P);             // slots it evicts (fill <= P)
   const int nl = min(max(a.n_local, 0), min(kk, n));
   const int cand_slots = n - nl;
-  const int64_t ubase = (a.sp.tok_off[b] * g.L * g.Hkv + (int64_t)(l * g.Hkv + kvh) * n) * kDists;
+  const int64_t ubase = (a.sp.tok_off[b] * g.L * g.Hkv + (int64_t)(l * g.Hkv + kvh) * logit_rows(n)) * kDists;
   const float* x = a.sp.logits + ubase;
 
   if (n == 0) {
@@ -652,7 +652,90 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void f
   }
 }
 
+template <int KCAP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void finish_kernel(FinishArgs a) {
+  __shared__ FinishLds<KCAP> lds;
+  const int upr = a.g.L * a.g.Hkv;
+  const int rank = blockIdx.x / upr;
+  const int rem = blockIdx.x - rank * upr;
+  const int l = rem / a.g.Hkv;
+  finish_unit<KCAP>(a, rank, l, rem - l * a.g.Hkv, lds);
+}
+
+// The whole scan of one unit per block: the four waves compute the logits of a quarter
+// of the unit's 16-token steps each on the matrix cores (logit_mfma.h), staging them in
+// the selection's LDS (free until the selection starts) and writing them out in blocks;
+// the block combines the row maxima and then selects from those logits while they are
+// still in the caches, instead of a second kernel reading them back from HBM.
+template <int D, int KCAP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void fused_scan_kernel(ScanArgs s,
+                                                                                                FinishArgs f) {
+  static_assert(sizeof(FinishLds<KCAP>) >= 4 * kStageBytes, "logit staging exceeds the selection LDS");
+  __shared__ FinishLds<KCAP> lds;
+  __shared__ float s_mw[4][kDists];
+  const Geo& g = s.g;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // wave-uniform (a scalar register): the logit loop's bounds and page ids derive from it
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int upr = g.L * g.Hkv;
+  const int rank = blockIdx.x / upr;
+  const int rem = blockIdx.x - rank * upr;
+  const int l = rem / g.Hkv;
+  const int kvh = rem - l * g.Hkv;
+  const int b = s.sp.order[rank];
+  if (!s.sp.flags[b]) {
+    const int n = s.sp.n_tok[b];
+    const int r = g.req_ids[b];
+    const int32_t* pt = g.page_table + (int64_t)r * g.max_pages;
+    MfmaSummaries<D> A;
+    A.load(s, r, l, kvh, lane);
+    const int steps = (n + kMfmaTok - 1) / kMfmaTok;
+    const int s0 = steps * wave / 4;
+    const int s1 = steps * (wave + 1) / 4;
+    float* lg = s.sp.logits + (s.sp.tok_off[b] * g.L * g.Hkv + (int64_t)(l * g.Hkv + kvh) * logit_rows(n)) * kDists;
+    float* stage = reinterpret_cast<float*>(&lds) + wave * (kStageBytes / sizeof(float));
+    f32x4_t mx = mfma_logit_steps<D>(s, A, pt, n, l, kvh, s0, s1, lg, stage, lane);
+    // max over the 16 tokens (lanes) of each row group: lanes 0 and 16 end with rows 0..3, 4..7
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = mx[i];
+      v = fmaxf(v, __shfl_xor(v, 1, 64));
+      v = fmaxf(v, __shfl_xor(v, 2, 64));
+      v = fmaxf(v, __shfl_xor(v, 4, 64));
+      v = fmaxf(v, __shfl_xor(v, 8, 64));
+      mx[i] = v;
+    }
+    if (lane == 0 || lane == 16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_mw[wave][4 * (lane >> 4) + i] = mx[i];
+    }
+    __syncthreads();
+    if (tid < kDists) {
+      const float m = fmaxf(fmaxf(s_mw[0][tid], s_mw[1][tid]), fmaxf(s_mw[2][tid], s_mw[3][tid]));
+      const int h = kvh * kGroup + (tid >> 1);
+      s.sp.stats[((((int64_t)b * g.L + l) * g.Hq + h) * 2 + (tid & 1)) * 2] = m;
+    }
+    __syncthreads();  // the unit's logits and maxima are visible to the whole block
+  }
+  finish_unit<KCAP>(f, rank, l, kvh, lds);
+}
+
 }  // namespace
+
+hipError_t launch_fused_scan(const ScanArgs& s, const FinishArgs& f, hipStream_t st) {
+  const int64_t units = (int64_t)f.g.n_req * f.g.L * f.g.Hkv;
+  const dim3 grid((unsigned)units), block(256);
+  const bool big = keep_cap(f.g.P) != 512;
+  if (f.g.d == 128) {
+    if (big) hipLaunchKernelGGL((fused_scan_kernel<128, 1024>), grid, block, 0, st, s, f);
+    else hipLaunchKernelGGL((fused_scan_kernel<128, 512>), grid, block, 0, st, s, f);
+  } else {
+    if (big) hipLaunchKernelGGL((fused_scan_kernel<64, 1024>), grid, block, 0, st, s, f);
+    else hipLaunchKernelGGL((fused_scan_kernel<64, 512>), grid, block, 0, st, s, f);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_finish(const FinishArgs& a, hipStream_t st) {
   const int64_t units = (int64_t)a.g.n_req * a.g.L * a.g.Hkv;

@@ -13,17 +13,22 @@ constexpr int kDists = 8;          // 4 query heads per KV head x 2 summaries
 constexpr int kGroup = 4;          // query heads per KV head
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kReqFields = 8;      // per-request int32 fields of the compaction plan
+constexpr int kLogitAlign = 16;    // each unit's logit rows start on a 512-byte boundary
+
+// Token rows a unit of n candidate slots takes in the logit scratch: n rounded up to a
+// multiple of kLogitAlign, so that every 16-token store covers whole cache lines.
+__host__ __device__ inline int64_t logit_rows(int64_t n) { return (n + kLogitAlign - 1) / kLogitAlign * kLogitAlign; }
 
 // ----------------------------------------------------------------------------- scratch
 // One caller buffer, carved into 256-byte aligned regions.  The scan fills the
 // request plan, logits and statistics; the compaction reads them.
 struct ScratchLayout {
-  size_t tok_off;   // int64 [n_req]  first candidate token of each entry
+  size_t tok_off;   // int64 [n_req]  first logit row of each entry (multiple of 16)
   size_t n_tok;     // int32 [n_req]  candidate slots n (0 when over budget)
   size_t order;     // int32 [n_req]  entries by n descending (ties by index)
   size_t flags;     // int32 [n_req]  GP_REQ_OVERFLOW when over budget
   size_t stats;     // float [n_req][L][Hq][2][2]  max logit, sum exp
-  size_t logits;    // float [tokens][L][Hkv][8] (per unit: [n][8], token-major)
+  size_t logits;    // float [rows][L][Hkv][8] (per unit: [logit_rows(n)][8], token-major)
   size_t ev;        // int32 [n_req][L][Hkv][P]  slots a compaction evicts, ascending
   size_t e_unit;    // int32 [n_req][L][Hkv]     first of them (n if none)
   size_t req;       // int32 [n_req][kReqFields]  first changed slot, copy-on-write plan
@@ -52,7 +57,8 @@ inline ScratchLayout scratch_layout(const gp_kv& kv, int32_t n_req, int64_t max_
   s.order = take(nr * sizeof(int32_t));
   s.flags = take(nr * sizeof(int32_t));
   s.stats = take(nr * kv.L * kv.Hq * 4 * sizeof(float));
-  s.logits = take(tok * kv.L * kv.Hkv * kDists * sizeof(float));
+  // Padding adds fewer than kLogitAlign rows per entry.
+  s.logits = take((tok + nr * (kLogitAlign - 1)) * kv.L * kv.Hkv * kDists * sizeof(float));
   s.ev = take(units * kv.P * sizeof(int32_t));
   s.e_unit = take(units * sizeof(int32_t));
   s.req = take(nr * kReqFields * sizeof(int32_t));
@@ -135,6 +141,24 @@ struct FinishArgs {
   float* stats_out;
 };
 hipError_t launch_finish(const FinishArgs& a, hipStream_t st);
+
+// Arguments of the scan's logit kernels.
+struct ScanArgs {
+  Geo g;
+  ScratchPtrs sp;
+  int64_t max_tokens;
+  const float* sum_s;
+  const float* sum_l;
+  const float* rope_cos;
+  const float* rope_sin;
+  int32_t rope_max_pos;
+  const int32_t* pos;
+  float scale;
+  int32_t* ws_out;
+};
+// bf16 keys in pages of a multiple of 16 tokens: logits and working sets in one kernel.
+constexpr int kFusedPageMultiple = 16;
+hipError_t launch_fused_scan(const ScanArgs& s, const FinishArgs& f, hipStream_t st);
 
 hipError_t launch_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_req, int32_t L,
                          int32_t Hq, int32_t tau, const gp_pages& pg, int32_t P, int32_t policy,

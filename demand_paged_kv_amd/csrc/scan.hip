@@ -3,20 +3,22 @@
 // (GrowPage review on evolve.pub, "Summary": compare the Top-p attention working-set
 // sizes induced by the short- and long-timescale summaries, kept pre-RoPE.)
 //
-// Three launches (the third, finish_kernel, lives in finish.hip):
-//   plan_kernel    1 block: candidate slots n of every batch entry, token offsets into
-//                  the scratch, and a longest-first order of the entries.
-//   logit_kernel   one wave per (entry, layer, KV head) "unit", launched longest-first.
-//                  The wave streams the unit's K rows through the page table once;
-//                  16 lanes share a token row (each holds D/16 contiguous elements), every
-//                  lane keeps the matching slices of all 8 rotated summaries (4 query heads
-//                  x 2 timescales) in registers, and a DPP transpose-reduce (3 steps within
-//                  each 8-lane half, one across the halves) leaves lane j with the logit of
-//                  summary j mod 8 for its token.  Logits go to the scratch ([unit][n][8]
-//                  float32: one wave step writes 128 contiguous bytes), the running max to
-//                  the statistics.
-//   finish_kernel  one block per unit: exact Top-p working sets of the 8 logit rows and
-//                  the unit's keep-set, from two reads of the logits.
+// plan_kernel    1 block: candidate slots n of every batch entry, scratch offsets and a
+//                longest-first order of the entries.
+// Then, for bf16 keys in pages of a multiple of 16 tokens, fused_scan_kernel (finish.hip):
+// one block per (entry, layer, KV head) "unit" computes the unit's logits on the matrix
+// cores (logit_mfma.h) and selects from them.  Otherwise two kernels:
+//   logit_kernel   one wave per unit, launched longest-first.  The wave streams the
+//                  unit's K rows through the page table once; 16 lanes share a token row
+//                  (each holds D/16 contiguous elements), every lane keeps the matching
+//                  slices of all 8 rotated summaries (4 query heads x 2 timescales) in
+//                  registers, and a DPP transpose-reduce (3 steps within each 8-lane half,
+//                  one across the halves) leaves lane j with the logit of summary j mod 8
+//                  for its token.  Logits go to the scratch ([unit][n'][8] float32, n'
+//                  = n rounded up to 16: one wave step writes 128 contiguous bytes), the
+//                  running max to the statistics.
+//   finish_kernel  one block per unit (finish.hip): exact Top-p working sets of the 8
+//                  logit rows and the unit's keep-set, from two reads of the logits.
 #include "device_util.h"
 #include "gp_internal.h"
 #include "kv_chunk.h"
@@ -24,31 +26,20 @@
 namespace gp {
 namespace {
 
-struct ScanArgs {
-  Geo g;
-  ScratchPtrs sp;
-  int64_t max_tokens;
-  const float* sum_s;
-  const float* sum_l;
-  const float* rope_cos;
-  const float* rope_sin;
-  int32_t rope_max_pos;
-  const int32_t* pos;
-  float scale;
-  int32_t* ws_out;
-};
-
 // ----------------------------------------------------------------------------- plan
 constexpr int kPlanLds = 8192;
 
 __global__ __launch_bounds__(1024) void plan_kernel(ScanArgs a) {
   __shared__ int tmp[16];
-  __shared__ long long carry_s;
+  __shared__ long long carry_s, carry_pad_s;
   __shared__ int nvals[kPlanLds];
   const int tid = threadIdx.x;
   const Geo& g = a.g;
-  if (tid == 0) carry_s = 0;
+  if (tid == 0) carry_s = carry_pad_s = 0;
   __syncthreads();
+  // An entry overflows when the candidate tokens up to and including it exceed
+  // max_tokens; its logit rows start at the padded running sum (logit_rows), which the
+  // scratch sizes for max_tokens plus the padding of every entry.
   for (int base = 0; base < g.n_req; base += 1024) {
     const int b = base + tid;
     int n = 0;
@@ -56,18 +47,23 @@ __global__ __launch_bounds__(1024) void plan_kernel(ScanArgs a) {
       const int r = g.req_ids[b];
       n = g.n_alloc[r] * g.P + g.fill[r];
     }
-    int total = 0;
+    int total = 0, total_pad = 0;
     const int ex = block_exscan_1024(n, tmp, &total);  // fits int: per chunk < 2^31 tokens
+    const int ex_pad = block_exscan_1024((int)logit_rows(n), tmp, &total_pad);
     const long long off = carry_s + ex;
+    const long long off_pad = carry_pad_s + ex_pad;
     if (b < g.n_req) {
       const bool over = off + n > a.max_tokens;
-      a.sp.tok_off[b] = over ? 0 : off;
+      a.sp.tok_off[b] = over ? 0 : off_pad;
       a.sp.n_tok[b] = over ? 0 : n;
       a.sp.flags[b] = over ? GP_REQ_OVERFLOW : 0;
       if (b < kPlanLds) nvals[b] = over ? -1 : n;
     }
     __syncthreads();
-    if (tid == 0) carry_s += total;
+    if (tid == 0) {
+      carry_s += total;
+      carry_pad_s += total_pad;
+    }
     __syncthreads();
   }
   // Longest-first order (rank sort, ties by batch index) so long units start first.
@@ -177,7 +173,7 @@ __global__ __launch_bounds__(64) void logit_kernel(ScanArgs a) {
   }
 
   const int64_t unit_base =
-      (a.sp.tok_off[b] * g.L * g.Hkv + (int64_t)(l * g.Hkv + kvh) * n) * kDists;
+      (a.sp.tok_off[b] * g.L * g.Hkv + (int64_t)(l * g.Hkv + kvh) * logit_rows(n)) * kDists;
   float* lg = a.sp.logits + unit_base + js + tl * kDists;  // token-major: [n][8]
   const bool writer = j < 8;
   const char* kb = reinterpret_cast<const char*>(g.k) + ((int64_t)l * g.s_layer + (int64_t)kvh * g.s_head) * E +
@@ -298,13 +294,14 @@ hipError_t launch_scan(const Geo& g, const ScratchPtrs& sp, int64_t max_tokens,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t units = (int64_t)g.n_req * g.L * g.Hkv;
+  FinishArgs f{g, sp, top_p, n_local, ws_out, stats_out};
+  if (g.dtype == GP_BF16 && g.P % kFusedPageMultiple == 0) return launch_fused_scan(a, f, st);
   if (g.dtype == GP_BF16) {
     e = g.d == 128 ? launch_logits<true, 128>(a, units, st) : launch_logits<true, 64>(a, units, st);
   } else {
     e = g.d == 128 ? launch_logits<false, 128>(a, units, st) : launch_logits<false, 64>(a, units, st);
   }
   if (e != hipSuccess) return e;
-  FinishArgs f{g, sp, top_p, n_local, ws_out, stats_out};
   return launch_finish(f, st);
 }
 
