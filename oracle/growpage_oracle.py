@@ -48,6 +48,12 @@ Readings taken where the pages are silent (each repeated where it is used):
       the end of the step.  An empty stack turns a grow into a compaction (status
       GROW_DENIED); a request whose copy-on-write demand exceeds the stack is left
       untouched (status DEFERRED).
+  R16 SHRINK ablation [same page, "Strengths", item "Frequency-matched causal
+      ablations": SHRINK isolates the cost of irreversible shrinking]: grow iff
+      delta > tau as GrowPage; every other request at its boundary with A >= 2
+      keeps k = (A-1)*P slots by R6's rule in pages 0..A-2, drops its reference to
+      allocation page A-1 and moves its write page into that page-table slot; with
+      A < 2 it compacts in place.
 """
 from __future__ import annotations
 
@@ -60,6 +66,7 @@ import numpy as np
 NEAR_TIE = 1.0e-5          # cumulative-mass / relative-importance band for near-ties
 DECISION_COMPACT = 0
 DECISION_GROW = 1
+DECISION_SHRINK = 2
 REQ_GROW_DENIED = 1
 REQ_DEFERRED = 2
 REQ_NOT_AT_BOUNDARY = 4
@@ -165,7 +172,7 @@ def decide(ws: np.ndarray, wl: np.ndarray, tau: int) -> tuple:
     return delta, (DECISION_GROW if delta > tau else DECISION_COMPACT)
 
 
-POLICIES = ("growpage", "random", "inverse", "always_compact")
+POLICIES = ("growpage", "random", "inverse", "always_compact", "shrink")
 
 
 def policy_decision(delta: int, tau: int, policy: str = "growpage", u: float = 0.0,
@@ -176,9 +183,14 @@ def policy_decision(delta: int, tau: int, policy: str = "growpage", u: float = 0
     GrowPage differ from Zipage?": a fixed per-request budget never grows].  Readings: growpage grows iff
     delta > tau (R2); inverse grows iff -delta > tau; random grows iff the request's
     uniform draw u (an input, float32) is below grow_prob (float32); always_compact
-    never grows."""
+    never grows.  shrink [same item: SHRINK isolates the cost of irreversible shrinking]:
+    reading R16, grows iff delta > tau like GrowPage and otherwise shrinks the allocation
+    by one page (boundary_step turns a shrink of a one-page allocation into an in-place
+    compaction)."""
     if policy == "growpage":
         return DECISION_GROW if delta > tau else DECISION_COMPACT
+    if policy == "shrink":
+        return DECISION_GROW if delta > tau else DECISION_SHRINK
     if policy == "inverse":
         return DECISION_GROW if -delta > tau else DECISION_COMPACT
     if policy == "random":
@@ -325,7 +337,12 @@ def boundary_step(wl, sum_s: np.ndarray, sum_l: np.ndarray, params: dict) -> Ste
     sum_s/sum_l [B][L][Hq][d] float32 are the summaries at the boundary.  Follows
     [Summary] and [Abstract] under readings R1-R7.  Inputs are not modified.  Optional
     params "policy", "rand_u" ([B] float32) and "grow_prob" select a decision policy
-    (policy_decision); the default is GrowPage's own rule.
+    (policy_decision); the default is GrowPage's own rule.  Under "shrink" (reading R16)
+    a request at its boundary that does not grow -- by decision or because its grow is
+    denied -- and holds A >= 2 allocation pages keeps (A - 1) P slots (same keep-set
+    rule), compacted into pages 0..A-2; allocation page A-1 loses this request's
+    reference (pushed with the other freed pages if that was the last one) and the write
+    page takes its place in the page table (index A-1).  With A < 2 it compacts in place.
     """
     B, L, Hq, Hkv, P = wl.B, wl.L, wl.Hq, wl.Hkv, wl.P
     G = Hq // Hkv
@@ -389,6 +406,11 @@ def boundary_step(wl, sum_s: np.ndarray, sum_l: np.ndarray, params: dict) -> Ste
             decision[b] = DECISION_COMPACT
             status[b] |= REQ_GROW_DENIED
             counters["grow_denied"] += 1
+    if policy == "shrink":  # every request at its boundary that does not grow shrinks (R16)
+        for b in range(B):
+            if at_boundary[b] and decision[b] != DECISION_GROW:
+                decision[b] = DECISION_SHRINK if A[b] >= 2 else DECISION_COMPACT
+    counters["shrinks"] = 0
 
     # Keep-sets, copy-on-write and compaction for compacting requests, batch order.
     evicted, near, imps, k_new, v_new, cow = {}, {}, {}, {}, {}, []
@@ -397,9 +419,10 @@ def boundary_step(wl, sum_s: np.ndarray, sum_l: np.ndarray, params: dict) -> Ste
     for b in range(B):
         n = int(wl.n_alloc[b]) * P + int(wl.fill[b])
         e_req[b] = n
-        if not at_boundary[b] or decision[b] != DECISION_COMPACT:
+        if not at_boundary[b] or decision[b] == DECISION_GROW:
             continue
-        k = int(wl.n_alloc[b]) * P
+        shrink = decision[b] == DECISION_SHRINK
+        k = (int(wl.n_alloc[b]) - (1 if shrink else 0)) * P
         ev = np.zeros((L, Hkv, n - k), np.int64)
         nt = np.zeros((L, Hkv), bool)
         im = np.zeros((L, Hkv, n))
@@ -413,9 +436,9 @@ def boundary_step(wl, sum_s: np.ndarray, sum_l: np.ndarray, params: dict) -> Ste
                 if evd.size:
                     e_req[b] = min(e_req[b], int(evd[0]))
         evicted[b], near[b], imps[b] = ev, nt, im
-        # Pages of the allocation that change: j with (j+1)*P > e (R7).
+        # Pages of the allocation that change: j < k / P with (j+1)*P > e (R7).
         j0 = int(e_req[b]) // P
-        need = [j for j in range(j0, int(wl.n_alloc[b])) if rc_snap[table[b, j]] > 1]
+        need = [j for j in range(j0, k // P) if rc_snap[table[b, j]] > 1]
         if len(need) > top:
             status[b] |= REQ_DEFERRED
             counters["deferred"] += 1
@@ -439,6 +462,15 @@ def boundary_step(wl, sum_s: np.ndarray, sum_l: np.ndarray, params: dict) -> Ste
         k_new[b], v_new[b] = kn, vn
         fill[b] = 0
         counters["compacts"] += 1
+        if shrink:  # release allocation page A-1; the write page moves into its slot
+            a_old = int(A[b])
+            old = int(table[b, a_old - 1])
+            refcount[old] -= 1
+            if refcount[old] == 0:
+                freed.append(old)
+            table[b, a_old - 1] = table[b, a_old]
+            A[b] = a_old - 1
+            counters["shrinks"] += 1
 
     for pg in sorted(freed):
         stack[top] = pg

@@ -39,6 +39,11 @@ MUTATIONS = {
     "gqa_heads_strided": ("scan_request", "                h = g * G + j\n", "                h = j * Hkv + g\n"),
     "append_overfills": ("append_token", "if int(state.fill[b]) >= state.P:", "if int(state.fill[b]) > state.P:"),
     "positions_frozen": ("decode_step", "state.pos = state.pos + 1", "state.pos = state.pos + 0"),
+    "shrink_keeps_whole_allocation": ("boundary_step", "k = (int(wl.n_alloc[b]) - (1 if shrink else 0)) * P",
+                                      "k = int(wl.n_alloc[b]) * P"),
+    "shrink_releases_write_page": ("boundary_step", "old = int(table[b, a_old - 1])", "old = int(table[b, a_old])"),
+    "shrink_on_one_page": ("boundary_step", "DECISION_SHRINK if A[b] >= 2 else DECISION_COMPACT",
+                           "DECISION_SHRINK if A[b] >= 1 else DECISION_COMPACT"),
     "attention_scale_dropped": ("decode_attention", "softmax_stats(logits(qt[None, :], kf))",
                                 "softmax_stats(logits(qt[None, :], kf) * math.sqrt(d))"),
     "attention_query_not_rotated": ("decode_attention", "qt = rope_rotate(qf[l, h], cos_row, sin_row)",

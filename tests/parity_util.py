@@ -314,15 +314,18 @@ def compare_sampled(wl, batch_idx, st, out, params: dict) -> Report:
     return rep
 
 
-def check_pool_shared(st, before: dict, out, n_req: int, P: int, tau: int):
+def check_pool_shared(st, before: dict, out, n_req: int, P: int, tau: int, shrink: bool = False):
     """Whole-batch page-state invariants with shared pages, from the pages' allocation
     rules as read here: grows pop the stack top in batch order (denied when it is empty or
     the page-table row is full); then compacting requests, in batch order, take fresh
     pages for the shared pages (refcount > 1 before the step) from the first page their
     compaction changes on, or are deferred untouched when the stack is short; pages whose
-    refcount reaches 0 are pushed in ascending order.  Replayed from the GPU's own deltas
-    and evicted slots (a consistency check of the page logic; the scan and keep-sets are
-    checked against the oracle elsewhere)."""
+    refcount reaches 0 are pushed in ascending order.  With ``shrink`` (the SHRINK policy)
+    every request at its boundary that does not grow and holds two or more allocation
+    pages keeps one page fewer, drops its reference to its last allocation page and moves
+    its write page into that slot.  Replayed from the GPU's own deltas and evicted slots (a
+    consistency check of the page logic; the scan and keep-sets are checked against the
+    oracle elsewhere)."""
     delta = out.delta.cpu().numpy()[:n_req]
     dec = out.decision.cpu().numpy()[:n_req]
     status = out.status.cpu().numpy()[:n_req]
@@ -355,10 +358,14 @@ def check_pool_shared(st, before: dict, out, n_req: int, P: int, tau: int):
     for b in range(n_req):
         if fill[b] != P or want_dec[b] == O.DECISION_GROW:
             continue
+        sh = shrink and A[b] >= 2
+        if sh:
+            want_dec[b] = O.DECISION_SHRINK
         n = int(A[b]) * P + P
-        e = ev[b][..., : P]
+        k = (int(A[b]) - (1 if sh else 0)) * P
+        e = ev[b][..., : n - k]
         e_r = int(e.min()) if e.size else n
-        need = [j for j in range(e_r // P, int(A[b])) if rc0[table[b, j]] > 1]
+        need = [j for j in range(e_r // P, k // P) if rc0[table[b, j]] > 1]
         if len(need) > top:
             want_status[b] |= O.REQ_DEFERRED
             continue
@@ -371,6 +378,13 @@ def check_pool_shared(st, before: dict, out, n_req: int, P: int, tau: int):
             if rc[old] == 0:
                 freed.append(old)
         fill[b] = 0
+        if sh:
+            old = table[b, A[b] - 1]
+            rc[old] -= 1
+            if rc[old] == 0:
+                freed.append(old)
+            table[b, A[b] - 1] = table[b, A[b]]
+            A[b] -= 1
     for pg in sorted(freed):
         stack[top] = pg
         top += 1

@@ -501,8 +501,12 @@ def test_policy_rules():
     assert O.policy_decision(0, 0, "growpage") == O.policy_decision(0, 0, "inverse") == O.DECISION_COMPACT
     for u, rho, want in ((0.0, 0.0, 0), (0.999, 1.0, 1), (0.3, 0.3, 0), (0.29, 0.3, 1)):
         assert O.policy_decision(100, 0, "random", u, rho) == want
+    for d in (-5, -1, 0, 1, 7):
+        for tau in (0, 2):
+            want = O.DECISION_GROW if d > tau else O.DECISION_SHRINK
+            assert O.policy_decision(d, tau, "shrink") == want
     with pytest.raises(ValueError):
-        O.policy_decision(1, 0, "shrink")
+        O.policy_decision(1, 0, "grow_always")
 
 
 def test_boundary_step_follows_the_policy():
@@ -517,6 +521,89 @@ def test_boundary_step_follows_the_policy():
     u = np.array([0.1, 0.9, 0.5, 0.2, 0.7, 0.05], np.float32)
     rnd = O.boundary_step(wl, wl.sum_s, wl.sum_l, dict(wl.params, policy="random", rand_u=u, grow_prob=0.3))
     assert np.array_equal(rnd.decision, (u < np.float32(0.3)).astype(rnd.decision.dtype))
+
+
+def _shrink_checks(wl, res, b, n_local):
+    """A request that shrank (R16): one allocation page fewer, the write page in the
+    released page's table slot, (A-1) P slots kept by the keep-set rule and packed in
+    slot order, the local window kept, the write page emptied."""
+    A, P, n = int(wl.n_alloc[b]), wl.P, wl.n(b)
+    assert res.decision[b] == O.DECISION_SHRINK and res.n_alloc[b] == A - 1 and res.fill[b] == 0
+    assert res.page_table[b, A - 1] == wl.page_table[b, A]
+    k = (A - 1) * P
+    assert res.evicted[b].shape[-1] == n - k and res.k_new[b].shape[2] == k
+    for l in range(wl.L):
+        for g in range(wl.Hkv):
+            ev = res.evicted[b][l, g]
+            assert O.keep_set_valid(ev, res.imp[b][l, g], k, n_local)
+            assert ev.size == 0 or ev.max() < n - min(n_local, k)
+            kept = np.setdiff1d(np.arange(n), ev)
+            assert np.array_equal(res.k_new[b][l, g], wl.k_rows[b][l, g][kept])
+            assert np.array_equal(res.v_new[b][l, g], wl.v_rows[b][l, g][kept])
+
+
+def test_shrink_releases_one_page():
+    """SHRINK (R16) against GrowPage on the same batch: same deltas and grows; every
+    other request at its boundary with two or more allocation pages shrinks by one, and
+    a one-page allocation compacts in place; an unshared released page is pushed."""
+    n_local = 8
+    wl = SW.direct_case(seed=81, B=10, L=2, Hq=8, Hkv=2, d=64, P=16, ctx=(8, 200), grow_frac=0.4,
+                        spare_pages=64, params=dict(SW.PARAMS_DEFAULT, n_local=n_local))
+    base = O.boundary_step(wl, wl.sum_s, wl.sum_l, wl.params)
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, dict(wl.params, policy="shrink"))
+    assert np.array_equal(res.delta, base.delta)
+    kinds = set()
+    for b in range(wl.B):
+        A = int(wl.n_alloc[b])
+        if base.decision[b] == O.DECISION_GROW:
+            assert res.decision[b] == O.DECISION_GROW and res.n_alloc[b] == A + 1
+            kinds.add("grow")
+        elif A >= 2:
+            _shrink_checks(wl, res, b, n_local)
+            released = int(wl.page_table[b, A - 1])
+            assert res.refcount[released] == 0 and released in res.free_stack[: res.free_top]
+            kinds.add("shrink")
+        else:
+            assert res.decision[b] == O.DECISION_COMPACT and res.n_alloc[b] == A
+            assert res.k_new[b].shape[2] == A * wl.P
+            kinds.add("compact")
+    assert kinds == {"grow", "shrink", "compact"}
+    assert res.counters["shrinks"] == int(np.sum(res.decision == O.DECISION_SHRINK))
+    assert res.counters["freed_pages"] == res.counters["shrinks"]
+    # pushes come after the pops, in ascending page id
+    grows = int(np.sum(res.decision == O.DECISION_GROW))
+    pushed = res.free_stack[wl.free_top - grows: res.free_top]
+    assert pushed.size == res.counters["shrinks"] and np.all(np.diff(pushed) > 0)
+    _pool_invariants(res, wl)
+
+
+def test_shrink_keeps_shared_pages_alive():
+    """Four requests share a 3-page prefix and hold exactly those 3 pages: each shrink
+    drops one reference to shared page 2 (pushed only when the last one goes) and copies
+    on write the shared pages its compaction changes."""
+    wl = SW.direct_case(seed=82, B=4, grow_frac=0.0, prefix_groups=1, prefix_pages=3, ctx=(20, 40),
+                        spare_pages=40, params=dict(SW.PARAMS_DEFAULT, n_local=8))
+    assert np.all(wl.n_alloc == 3) and wl.refcount[wl.page_table[0, 2]] == 4
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, dict(wl.params, policy="shrink"))
+    shared2 = int(wl.page_table[0, 2])
+    for b in range(wl.B):
+        _shrink_checks(wl, res, b, 8)
+        for (bb, j, old, new) in res.cow:
+            assert j < 2
+    assert res.refcount[shared2] == 0 and shared2 in res.free_stack[: res.free_top]
+    assert res.counters["cow_pages"] > 0
+    _pool_invariants(res, wl)
+
+
+def test_shrink_after_a_denied_grow():
+    """Under SHRINK a grow the free stack cannot serve shrinks instead (flagged)."""
+    wl = SW.direct_case(seed=12, B=6, grow_frac=1.0, spare_pages=3)
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, dict(wl.params, policy="shrink"))
+    denied = [b for b in range(wl.B) if res.status[b] & O.REQ_GROW_DENIED]
+    assert denied
+    for b in denied:
+        assert res.decision[b] == (O.DECISION_SHRINK if wl.n_alloc[b] >= 2 else O.DECISION_COMPACT)
+    _pool_invariants(res, wl)
 
 
 # ----------------------------------------------------------------------------- decode attention
