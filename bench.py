@@ -334,11 +334,12 @@ def decode_loop(args):
 def policies(args):
     """The decode loop (128 requests x 36 layers from 1024-token prompts, --decode-steps
     steps) under each decision policy: GrowPage's own rule, RANDOM at GrowPage's measured
-    grow ratio (frequency-matched), INVERSE and ALWAYS_COMPACT.  Reports grow ratios and
-    pages in use at the end.  For GrowPage's run it also reports how the boundary signal
-    delta_t ranks against the change of the recent working set over the next h boundaries,
-    sum W_S(t+h) - sum W_L(t) (Spearman rho and sign agreement) -- a model-free analogue of
-    the pages' demand-prediction check (GrowPage review, "Key claims", Fig 6)."""
+    grow ratio (frequency-matched), INVERSE, ALWAYS_COMPACT and SHRINK.  Reports grow (and
+    shrink) ratios and pages in use at the end.  For GrowPage's run it also reports how
+    the boundary signal delta_t ranks against the change of the recent working set over
+    the next h boundaries, sum W_S(t+h) - sum W_L(t) (Spearman rho and sign agreement) --
+    a model-free analogue of the pages' demand-prediction check (GrowPage review, "Key
+    claims", Fig 6)."""
     import numpy as np
     import torch
     from scipy.stats import spearmanr
@@ -352,17 +353,17 @@ def policies(args):
     out = {}
     grow_ratio = None
     sig = None
-    for policy in ("growpage", "random", "inverse", "always_compact"):
+    for policy in ("growpage", "random", "inverse", "always_compact", "shrink"):
         spec = DecodeSpec(steps=steps)
         gen = DecodeLoopGen(spec, "cuda")
         st = gen.initial_state()
         eng = BoundaryEngine(st, spec.B, spec.B * (spec.prompt + spec.steps + spec.P),
-                             Bd.params_from(spec.params))
+                             Bd.params_from(dict(spec.params, policy=policy)))
         req = torch.arange(spec.B, dtype=torch.int32, device="cuda")
         rng = np.random.default_rng(spec.seed + 7)
         u = torch.zeros(spec.B, dtype=torch.float32, device="cuda")
         eng.set_policy(policy, u, grow_ratio or 0.0)
-        grows = denied = boundaries = 0
+        grows = denied = shrinks = boundaries = 0
         ws_s, ws_l, deltas = [], [], []
         t0 = time.time()
         for t in range(spec.steps):
@@ -377,6 +378,7 @@ def policies(args):
                 c = o.counters.cpu().numpy()
                 grows += int(c[0])
                 denied += int(c[2])
+                shrinks += int(c[8])
                 if policy == "growpage":
                     w = o.ws[: spec.B].to(torch.int64).sum(dim=(1, 2)).cpu().numpy()     # [B][2]
                     ws_s.append(w[:, 0])
@@ -388,6 +390,8 @@ def policies(args):
         out[policy] = {"grow_ratio": round(ratio, 4), "grows": grows, "grow_denied": denied,
                        "pages_in_use_end": pages, "boundaries": boundaries,
                        "wall_s": round(time.time() - t0, 2)}
+        if policy == "shrink":
+            out[policy]["shrink_ratio"] = round(shrinks / (boundaries * spec.B), 4)
         log(f"policy {policy}: grow ratio {ratio:.4f}, pages {pages}")
         if policy == "growpage":
             grow_ratio = ratio

@@ -17,9 +17,9 @@ LIB_PATH = os.path.join(HERE, "libgrowpage.so")
 GP_OK, GP_ERR_INVALID, GP_ERR_HIP, GP_ERR_SCRATCH, GP_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 GP_F32, GP_BF16 = 0, 1
 GP_REQ_GROW_DENIED, GP_REQ_DEFERRED, GP_REQ_NOT_AT_BOUNDARY, GP_REQ_OVERFLOW = 1, 2, 4, 8
-GP_DECISION_COMPACT, GP_DECISION_GROW = 0, 1
+GP_DECISION_COMPACT, GP_DECISION_GROW, GP_DECISION_SHRINK = 0, 1, 2
 COUNTER_NAMES = ("grows", "compacts", "grow_denied", "deferred", "cow_pages", "freed_pages",
-                 "moved_rows", "copied_rows")
+                 "moved_rows", "copied_rows", "shrinks")
 GP_NUM_COUNTERS = len(COUNTER_NAMES)
 
 EXPORTED = ("gp_abi_version", "gp_status_string", "gp_last_hip_error_string", "gp_update_summaries",
@@ -27,7 +27,7 @@ EXPORTED = ("gp_abi_version", "gp_status_string", "gp_last_hip_error_string", "g
             "gp_boundary_scan", "gp_decide", "gp_decide_policy", "gp_compact", "gp_compact_prepare",
             "gp_compact_move", "gp_append_kv", "gp_decode_attention")
 # decision policies (gp_decide_policy)
-POLICIES = {"growpage": 0, "random": 1, "inverse": 2, "always_compact": 3}
+POLICIES = {"growpage": 0, "random": 1, "inverse": 2, "always_compact": 3, "shrink": 4}
 
 
 class GrowPageError(RuntimeError):
@@ -36,7 +36,7 @@ class GrowPageError(RuntimeError):
 
 class Params(ctypes.Structure):
     _fields_ = [("beta_s", ctypes.c_float), ("beta_l", ctypes.c_float), ("top_p", ctypes.c_float),
-                ("tau", ctypes.c_int32), ("n_local", ctypes.c_int32)]
+                ("tau", ctypes.c_int32), ("n_local", ctypes.c_int32), ("shrink", ctypes.c_int32)]
 
 
 class KV(ctypes.Structure):
@@ -133,12 +133,13 @@ def _check(status: int, what: str):
         raise GrowPageError(f"{what}: {msg}")
 
 
-def params(beta_s=0.9, beta_l=0.999, top_p=0.9, tau=0, n_local=64) -> Params:
-    return Params(float(beta_s), float(beta_l), float(top_p), int(tau), int(n_local))
+def params(beta_s=0.9, beta_l=0.999, top_p=0.9, tau=0, n_local=64, shrink=0) -> Params:
+    return Params(float(beta_s), float(beta_l), float(top_p), int(tau), int(n_local), int(shrink))
 
 
 def params_from(d: dict) -> Params:
-    return params(d["beta_s"], d["beta_l"], d["top_p"], d["tau"], d["n_local"])
+    return params(d["beta_s"], d["beta_l"], d["top_p"], d["tau"], d["n_local"],
+                  1 if d.get("policy") == "shrink" else 0)
 
 
 def make_kv(k, v, L, Hq, Hkv, d, P, num_pages, dtype, strides=None) -> KV:

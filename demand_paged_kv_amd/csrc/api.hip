@@ -22,6 +22,7 @@ gp_status check_params(const gp_params* p) {
   if (!p) return GP_ERR_INVALID;
   if (!(p->beta_s > 0.f && p->beta_s <= 1.f) || !(p->beta_l > 0.f && p->beta_l <= 1.f)) return GP_ERR_INVALID;
   if (!(p->top_p == p->top_p) || p->n_local < 0) return GP_ERR_INVALID;
+  if (p->shrink != 0 && p->shrink != 1) return GP_ERR_INVALID;
   return GP_OK;
 }
 
@@ -139,7 +140,7 @@ gp_status gp_boundary_scan(const gp_kv* kv, const gp_pages* pages, const int32_t
   const Geo g = make_geo(kv, pages, req_ids, n_req);
   return from_hip(launch_scan(g, scratch_ptrs(scratch, lay), max_total_tokens, sum_s, sum_l, rope_cos,
                               rope_sin, rope_max_pos, pos, params->top_p, params->n_local,
-                              ws_out, stats_out, (hipStream_t)stream));
+                              params->shrink, ws_out, stats_out, (hipStream_t)stream));
 }
 
 gp_status gp_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_req, int32_t L,
@@ -148,6 +149,7 @@ gp_status gp_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_req, in
                     int32_t* counters_out, void* stream) {
   if (gp_status s = check_pages(pages, true)) return s;
   if (gp_status s = check_params(params)) return s;
+  if (params->shrink) return GP_ERR_INVALID;  // GrowPage's own rule never shrinks
   if (n_req < 0 || n_req > pages->max_req || L <= 0 || Hq <= 0 || P <= 0) return GP_ERR_INVALID;
   if (n_req == 0) return GP_OK;
   if (!ws || !req_ids || !decision_out || !delta_out || !status_out) return GP_ERR_INVALID;
@@ -163,7 +165,9 @@ gp_status gp_decide_policy(const int32_t* ws, const int32_t* req_ids, int32_t n_
                            int32_t* counters_out, void* stream) {
   if (gp_status s = check_pages(pages, true)) return s;
   if (gp_status s = check_params(params)) return s;
-  if (policy < GP_POLICY_GROWPAGE || policy > GP_POLICY_ALWAYS_COMPACT) return GP_ERR_INVALID;
+  if (policy < GP_POLICY_GROWPAGE || policy > GP_POLICY_SHRINK) return GP_ERR_INVALID;
+  // the scan sized the keep-sets for the policy: (A-1)*P slots exactly under SHRINK
+  if ((policy == GP_POLICY_SHRINK) != (params->shrink == 1)) return GP_ERR_INVALID;
   if (n_req < 0 || n_req > pages->max_req || L <= 0 || Hq <= 0 || P <= 0) return GP_ERR_INVALID;
   if (n_req == 0) return GP_OK;
   if (!ws || !req_ids || !decision_out || !delta_out || !status_out) return GP_ERR_INVALID;
@@ -198,7 +202,8 @@ gp_status gp_compact_prepare(const gp_kv* kv, const gp_pages* pages, const int32
   if (scratch_bytes < lay.total) return GP_ERR_SCRATCH;
   const Geo g = make_geo(kv, pages, req_ids, n_req);
   return from_hip(launch_compact_prepare(g, *pages, scratch_ptrs(scratch, lay), decision,
-                                         evicted_out, status_out, (hipStream_t)stream));
+                                         evicted_out, params->shrink ? 2 * kv->P : kv->P, status_out,
+                                         (hipStream_t)stream));
 }
 
 gp_status gp_compact_move(const gp_kv* kv, const gp_pages* pages, const int32_t* req_ids,

@@ -7,8 +7,9 @@
 //   (the keep-sets -- the n-k least important candidate slots of each (entry, layer,
 //    KV head) unit, ties to the older slot -- come from the scan's finish kernel)
 //   publish_kernel   copy the keep-sets of compacting entries to the caller (optional).
-//   req_kernel       per entry: first changed slot e (min over units), copy-on-write
-//                    demand = shared pages (refcount > 1) at index >= e / P.
+//   req_kernel       per entry: kept slots k (A*P, or (A-1)*P for a SHRINK decision),
+//                    first changed slot e (min over units), copy-on-write demand =
+//                    shared pages (refcount > 1) at index in [e / P, k / P).
 //   cowplan_kernel   1 block: greedy in batch order -- an entry whose demand fits the
 //                    free stack reserves its pops, otherwise it is deferred.
 //   cowassign_kernel per entry: assign popped pages in ascending page index, rewrite the
@@ -18,15 +19,17 @@
 //                    compaction, slot j <- slot kept[j] for j in [e, k), 128 destination
 //                    rows per step, all reads of a step before its writes (destinations
 //                    never exceed sources).
-//   finalize_kernel  1 block: refcount decrements of replaced pages, push the pages that
-//                    reached zero in ascending id order, empty the write pages, counters.
+//   finalize_kernel  1 block: refcount decrements of replaced pages and of the page each
+//                    SHRINK entry releases (its last allocation page, whose table slot
+//                    its write page takes), push the pages that reached zero in
+//                    ascending id order, empty the write pages, counters.
 #include "device_util.h"
 #include "gp_internal.h"
 
 namespace gp {
 namespace {
 
-enum { RQ_E = 0, RQ_NEED = 1, RQ_BASE = 2, RQ_STATE = 3, RQ_TOP = 4, RQ_N = kReqFields };
+enum { RQ_E = 0, RQ_NEED = 1, RQ_BASE = 2, RQ_STATE = 3, RQ_TOP = 4, RQ_K = 5, RQ_SHRINK = 6, RQ_N = kReqFields };
 enum { ST_NONE = 0, ST_PENDING = 1, ST_GO = 2, ST_DEFERRED = 3 };
 
 struct CompactArgs {
@@ -34,7 +37,7 @@ struct CompactArgs {
   gp_pages pg;
   ScratchPtrs sp;
   const uint8_t* decision;
-  int32_t unused;
+  int32_t ev_out_stride;  // evicted_out row length (P, or 2P under SHRINK)
   int32_t* evicted_out;
   int32_t* status_out;
   int32_t* counters_out;
@@ -51,7 +54,8 @@ __device__ __forceinline__ void unit_of_block(const Geo& g, const ScratchPtrs& s
 }
 
 __device__ __forceinline__ bool is_compacting(const CompactArgs& a, int b, int r) {
-  return a.sp.flags[b] == 0 && a.decision[b] == GP_DECISION_COMPACT && a.g.fill[r] == a.g.P;
+  const uint8_t d = a.decision[b];
+  return a.sp.flags[b] == 0 && (d == GP_DECISION_COMPACT || d == GP_DECISION_SHRINK) && a.g.fill[r] == a.g.P;
 }
 
 // ----------------------------------------------------------------------------- keep-set
@@ -65,8 +69,10 @@ __global__ __launch_bounds__(64) void publish_kernel(CompactArgs a) {
   const int r = g.req_ids[b];
   const int P = g.P;
   const bool comp = is_compacting(a, b, r);
-  const int E = comp ? a.sp.n_tok[b] - g.n_alloc[r] * P : 0;
-  for (int i = threadIdx.x; i < P; i += 64) a.evicted_out[u * P + i] = i < E ? a.sp.ev[u * P + i] : -1;
+  const int E = comp ? a.sp.n_tok[b] - kept_slots(g.n_alloc[r], P, a.decision[b] == GP_DECISION_SHRINK) : 0;
+  const int S = a.ev_out_stride;
+  for (int i = threadIdx.x; i < S; i += 64)
+    a.evicted_out[u * S + i] = i < E ? a.sp.ev[u * ev_stride(P) + i] : -1;
 }
 
 // ----------------------------------------------------------------------------- per entry
@@ -89,10 +95,11 @@ __global__ __launch_bounds__(256) void req_kernel(CompactArgs a) {
   __syncthreads();
   e = min(min(red[0], red[1]), min(red[2], red[3]));
   __syncthreads();
-  const int A = g.n_alloc[r];
+  const bool shrink = a.decision[b] == GP_DECISION_SHRINK;
+  const int k = kept_slots(g.n_alloc[r], g.P, shrink);
   const int32_t* pt = g.page_table + (int64_t)r * g.max_pages;
   int c = 0;
-  for (int j = e / g.P + tid; j < A; j += 256) c += a.pg.refcount[pt[j]] > 1 ? 1 : 0;
+  for (int j = e / g.P + tid; j < k / g.P; j += 256) c += a.pg.refcount[pt[j]] > 1 ? 1 : 0;
   c = wave_sum_int(c);
   if ((tid & 63) == 0) red[tid >> 6] = c;
   __syncthreads();
@@ -102,6 +109,8 @@ __global__ __launch_bounds__(256) void req_kernel(CompactArgs a) {
     rq[RQ_BASE] = 0;
     rq[RQ_STATE] = ST_PENDING;
     rq[RQ_TOP] = 0;
+    rq[RQ_K] = k;
+    rq[RQ_SHRINK] = shrink ? 1 : 0;
   }
 }
 
@@ -170,18 +179,18 @@ __global__ __launch_bounds__(256) void cowassign_kernel(CompactArgs a) {
   const int32_t* rq = a.sp.req + (int64_t)b * RQ_N;
   if (rq[RQ_STATE] != ST_GO || rq[RQ_NEED] == 0) return;
   const int r = g.req_ids[b];
-  const int A = g.n_alloc[r];
+  const int kp = rq[RQ_K] / g.P;  // allocation pages the compaction writes
   const int j0 = rq[RQ_E] / g.P;
   const int cbase = rq[RQ_BASE];
   const int ptop = rq[RQ_TOP];
   int32_t* pt = a.pg.page_table + (int64_t)r * g.max_pages;
   if (tid == 0) s_carry = 0;
   __syncthreads();
-  for (int jb = j0; jb < A; jb += 256) {
+  for (int jb = j0; jb < kp; jb += 256) {
     const int j = jb + tid;
     int old = -1;
     int flag = 0;
-    if (j < A) {
+    if (j < kp) {
       old = pt[j];
       flag = a.pg.refcount[old] > 1 ? 1 : 0;
     }
@@ -257,7 +266,7 @@ __global__ __launch_bounds__(256) void gather_kernel(CompactArgs a) {
   constexpr int ROWS = 128;            // destination rows per step
   constexpr int RPI = 256 / CPR;       // rows per instruction
   constexpr int NI = ROWS / RPI;       // instructions per step
-  __shared__ int s_thr[256];
+  __shared__ int s_thr[2 * 256];  // E <= 2P <= 512
   __shared__ int s_pt[kPtLds];
   const int tid = threadIdx.x;
   const int units = g.n_req * g.L * g.Hkv;
@@ -270,14 +279,14 @@ __global__ __launch_bounds__(256) void gather_kernel(CompactArgs a) {
   const int P = g.P;
   const int n = a.sp.n_tok[b];
   const int A = g.n_alloc[r];
-  const int k = A * P;
+  const int k = rq[RQ_K];
   const int E = n - k;
   const int64_t u = ((int64_t)b * g.L + l) * g.Hkv + kvh;
   const int e = a.sp.e_unit[u];
   if (e >= k) return;
   const int32_t* ptg = a.pg.page_table + (int64_t)r * g.max_pages;
   const bool pt_lds = A + 1 <= kPtLds;
-  for (int i = tid; i < E; i += 256) s_thr[i] = a.sp.ev[u * P + i] - i;
+  for (int i = tid; i < E; i += 256) s_thr[i] = a.sp.ev[u * ev_stride(P) + i] - i;
   if (pt_lds)
     for (int i = tid; i <= A; i += 256) s_pt[i] = ptg[i];
   __syncthreads();
@@ -315,7 +324,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(CompactArgs a) {
   __shared__ int tmp[16];
   __shared__ int s_carry;
   __shared__ unsigned long long s_moved;
-  __shared__ int s_comp, s_def;
+  __shared__ int s_comp, s_def, s_shrink;
   const int tid = threadIdx.x;
   const int ncow = a.sp.misc[0];
   const int words = g.num_pages / 32 + 1;
@@ -325,11 +334,26 @@ __global__ __launch_bounds__(1024) void finalize_kernel(CompactArgs a) {
     s_moved = 0;
     s_comp = 0;
     s_def = 0;
+    s_shrink = 0;
   }
   __syncthreads();
   for (int e = tid; e < ncow; e += 1024) {
     const int old = a.sp.cow[(int64_t)e * 2];
     if (atomicSub(&a.pg.refcount[old], 1) == 1) atomicOr(&a.sp.bitmap[old >> 5], 1u << (old & 31));
+  }
+  // SHRINK entries release their last allocation page (outside the copy-on-write range,
+  // so still the original page) and move their write page into its table slot.
+  for (int b = tid; b < g.n_req; b += 1024) {
+    const int32_t* rq = a.sp.req + (int64_t)b * RQ_N;
+    if (rq[RQ_STATE] != ST_GO || !rq[RQ_SHRINK]) continue;
+    const int r = g.req_ids[b];
+    const int A = a.pg.n_alloc[r];
+    int32_t* pt = a.pg.page_table + (int64_t)r * g.max_pages;
+    const int old = pt[A - 1];
+    if (atomicSub(&a.pg.refcount[old], 1) == 1) atomicOr(&a.sp.bitmap[old >> 5], 1u << (old & 31));
+    pt[A - 1] = pt[A];
+    a.pg.n_alloc[r] = A - 1;
+    atomicAdd(&s_shrink, 1);
   }
   __threadfence();
   __syncthreads();
@@ -360,7 +384,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(CompactArgs a) {
   for (long long uu = tid; uu < (long long)g.n_req * upr; uu += 1024) {
     const int b = (int)(uu / upr);
     if (a.sp.req[(int64_t)b * RQ_N + RQ_STATE] != ST_GO) continue;
-    const int k = g.n_alloc[g.req_ids[b]] * g.P;
+    const int k = a.sp.req[(int64_t)b * RQ_N + RQ_K];
     const int e = a.sp.e_unit[uu];
     if (e < k) moved += (unsigned long long)(k - e);
   }
@@ -375,6 +399,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(CompactArgs a) {
       a.counters_out[GP_CNT_FREED_PAGES] = s_carry;
       a.counters_out[GP_CNT_MOVED_ROWS] = (int32_t)min(s_moved, (unsigned long long)INT32_MAX);
       a.counters_out[GP_CNT_COPIED_ROWS] = (int32_t)min((long long)ncow * upr * g.P, (long long)INT32_MAX);
+      a.counters_out[GP_CNT_SHRINKS] = s_shrink;
     }
   }
 }
@@ -420,8 +445,8 @@ __global__ __launch_bounds__(256) void append_bump_kernel(Geo g, gp_pages pg, in
 
 hipError_t launch_compact_prepare(const Geo& g, const gp_pages& pg, const ScratchPtrs& sp,
                                   const uint8_t* decision, int32_t* evicted_out,
-                                  int32_t* status_out, hipStream_t st) {
-  CompactArgs a{g, pg, sp, decision, 0, evicted_out, status_out, nullptr};
+                                  int32_t evicted_stride, int32_t* status_out, hipStream_t st) {
+  CompactArgs a{g, pg, sp, decision, evicted_stride, evicted_out, status_out, nullptr};
   const unsigned units = (unsigned)((int64_t)g.n_req * g.L * g.Hkv);
   if (evicted_out) hipLaunchKernelGGL(publish_kernel, dim3(units), dim3(64), 0, st, a);
   hipLaunchKernelGGL(req_kernel, dim3((unsigned)g.n_req), dim3(256), 0, st, a);

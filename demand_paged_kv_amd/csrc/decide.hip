@@ -4,7 +4,9 @@
 //
 // delta_b = sum over layers and query heads of (W_short - W_long); grow iff delta > tau
 // (or, for the ablation policies the pages compare: iff -delta > tau, iff a uniform draw
-// falls below a grow probability, or never).
+// falls below a grow probability, or never).  Under SHRINK a request at its boundary
+// that does not grow and holds two or more allocation pages is decided SHRINK (the
+// compaction then keeps one page fewer).
 // Grows pop the device free stack in batch order: the eligible entries are ranked by a
 // block prefix sum and the first `free_top` of them receive free_stack[top-1-rank], so
 // page ids are deterministic without atomics.  One 1024-thread block: the batch is
@@ -57,11 +59,12 @@ __global__ __launch_bounds__(1024) void decide_kernel(DecideArgs a) {
   for (int base = 0; base < a.n_req; base += 1024) {
     const int b = base + tid;
     int eligible = 0, want = 0, st = 0, r = 0, A = 0;
+    bool over = false, at = false;
     if (b < a.n_req) {
       r = a.req_ids[b];
       A = a.pg.n_alloc[r];
-      const bool over = a.ws[(int64_t)b * per * 2] < 0;
-      const bool at = a.pg.fill[r] == a.P;
+      over = a.ws[(int64_t)b * per * 2] < 0;
+      at = a.pg.fill[r] == a.P;
       if (over) st |= GP_REQ_OVERFLOW;
       if (!at) st |= GP_REQ_NOT_AT_BOUNDARY;
       const int d = a.delta[b];
@@ -87,7 +90,9 @@ __global__ __launch_bounds__(1024) void decide_kernel(DecideArgs a) {
         a.pg.n_alloc[r] = A + 1;
         a.pg.fill[r] = 0;
       }
-      a.decision[b] = granted ? GP_DECISION_GROW : GP_DECISION_COMPACT;
+      uint8_t dec = granted ? GP_DECISION_GROW : GP_DECISION_COMPACT;
+      if (!granted && a.policy == GP_POLICY_SHRINK && !over && at && A >= 2) dec = GP_DECISION_SHRINK;
+      a.decision[b] = dec;
       a.status[b] = st;
     }
     __syncthreads();

@@ -41,11 +41,12 @@ constexpr float kBinsPerNat = 16.0f;
 // Crossing-bin elements held in LDS (all 8 rows): sized with the keep buffer so that a
 // block stays within 40 KB of LDS and four blocks (16 waves) share a CU.
 constexpr int cand_cap(int kcap) { return kcap == 512 ? 4864 : 3840; }
-// Threshold buffer of keep-set candidates: 512 keys for pages of up to 64 slots (a unit
-// evicts at most one page), 1024 above, so that after a compaction down to the E
-// smallest keys at least one more round of 256 new keys fits before the next one (and
-// three blocks still share a CU's LDS).
+// Threshold buffer of keep-set candidates: 512 keys for pages of up to 64 slots, 1024
+// above.  A unit evicts E <= 2P slots (2P when it shrinks by a page), and E + 256 <= the
+// capacity, so that after a compaction down to the E smallest keys at least one more
+// round of 256 new keys fits before the next one.
 constexpr int keep_cap(int P) { return P <= 64 ? 512 : 1024; }
+static_assert(2 * 64 + 256 <= 512 && 2 * 256 + 256 <= 1024, "keep buffer too small for 2P evictions");
 
 enum { MODE_DONE = 0, MODE_LDS = 1, MODE_GLOBAL = 2 };
 
@@ -376,8 +377,8 @@ __device__ __forceinline__ void finish_unit(const FinishArgs& a, int rank, int l
   const int n = a.sp.n_tok[b];
   const int r = g.req_ids[b];
   constexpr int kcap = KCAP;
-  const int kk = g.n_alloc[r] * g.P;                  // slots a compaction keeps
-  const int E = min(max(n - kk, 0), g.P);             // slots it evicts (fill <= P)
+  const int kk = kept_slots(g.n_alloc[r], g.P, a.shrink != 0);  // slots a compaction keeps
+  const int E = min(max(n - kk, 0), ev_stride(g.P));               // slots it evicts
   const int nl = min(max(a.n_local, 0), min(kk, n));
   const int cand_slots = n - nl;
   const int64_t ubase = (a.sp.tok_off[b] * g.L * g.Hkv + (int64_t)(l * g.Hkv + kvh) * logit_rows(n)) * kDists;
@@ -590,11 +591,11 @@ __device__ __forceinline__ void finish_unit(const FinishArgs& a, int rank, int l
     for (int j = tid; j < cnt; j += 256)
       if (kbuf[j] <= K) sel[atomicAdd(&s_c2, 1)] = (uint32_t)(kbuf[j] & 0xffffffffu);
     __syncthreads();
-    if (tid < E) {
-      const uint32_t s = sel[tid];
+    for (int t = tid; t < E; t += 256) {  // E <= 2P <= 512
+      const uint32_t s = sel[t];
       int rk = 0;
       for (int j = 0; j < E; ++j) rk += sel[j] < s ? 1 : 0;
-      a.sp.ev[u * g.P + rk] = (int)s;
+      a.sp.ev[u * ev_stride(g.P) + rk] = (int)s;
       if (rk == 0) a.sp.e_unit[u] = (int)s;
     }
   } else if (tid == 0) {

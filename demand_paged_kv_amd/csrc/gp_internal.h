@@ -19,6 +19,13 @@ constexpr int kLogitAlign = 16;    // each unit's logit rows start on a 512-byte
 // multiple of kLogitAlign, so that every 16-token store covers whole cache lines.
 __host__ __device__ inline int64_t logit_rows(int64_t n) { return (n + kLogitAlign - 1) / kLogitAlign * kLogitAlign; }
 
+// Evicted slots per unit: at the boundary n = (A+1)P, so a compaction evicts P slots,
+// or 2P when it shrinks the allocation by a page.
+__host__ __device__ inline int ev_stride(int P) { return 2 * P; }
+
+// Slots a compaction of a request with A allocation pages keeps.
+__host__ __device__ inline int kept_slots(int A, int P, bool shrink) { return (shrink && A >= 2 ? A - 1 : A) * P; }
+
 // ----------------------------------------------------------------------------- scratch
 // One caller buffer, carved into 256-byte aligned regions.  The scan fills the
 // request plan, logits and statistics; the compaction reads them.
@@ -29,7 +36,7 @@ struct ScratchLayout {
   size_t flags;     // int32 [n_req]  GP_REQ_OVERFLOW when over budget
   size_t stats;     // float [n_req][L][Hq][2][2]  max logit, sum exp
   size_t logits;    // float [rows][L][Hkv][8] (per unit: [logit_rows(n)][8], token-major)
-  size_t ev;        // int32 [n_req][L][Hkv][P]  slots a compaction evicts, ascending
+  size_t ev;        // int32 [n_req][L][Hkv][2P] slots a compaction evicts, ascending
   size_t e_unit;    // int32 [n_req][L][Hkv]     first of them (n if none)
   size_t req;       // int32 [n_req][kReqFields]  first changed slot, copy-on-write plan
   size_t cow;       // int32 [cow_cap][2]  (old page, new page)
@@ -59,7 +66,7 @@ inline ScratchLayout scratch_layout(const gp_kv& kv, int32_t n_req, int64_t max_
   s.stats = take(nr * kv.L * kv.Hq * 4 * sizeof(float));
   // Padding adds fewer than kLogitAlign rows per entry.
   s.logits = take((tok + nr * (kLogitAlign - 1)) * kv.L * kv.Hkv * kDists * sizeof(float));
-  s.ev = take(units * kv.P * sizeof(int32_t));
+  s.ev = take(units * ev_stride(kv.P) * sizeof(int32_t));
   s.e_unit = take(units * sizeof(int32_t));
   s.req = take(nr * kReqFields * sizeof(int32_t));
   s.cow_cap = (int64_t)(tok / (kv.P > 0 ? kv.P : 1) + nr);
@@ -129,14 +136,15 @@ hipError_t launch_ema(const void* q, int32_t q_dtype, int64_t sr, int64_t sl, in
 hipError_t launch_scan(const Geo& g, const ScratchPtrs& sp, int64_t max_tokens,
                        const float* sum_s, const float* sum_l, const float* rope_cos,
                        const float* rope_sin, int32_t rope_max_pos, const int32_t* pos,
-                       float top_p, int32_t n_local, int32_t* ws_out, float* stats_out,
-                       hipStream_t st);
+                       float top_p, int32_t n_local, int32_t shrink, int32_t* ws_out,
+                       float* stats_out, hipStream_t st);
 
 struct FinishArgs {
   Geo g;
   ScratchPtrs sp;
   float top_p;
   int32_t n_local;
+  int32_t shrink;   // keep-sets of kept_slots(A, P, shrink) slots
   int32_t* ws_out;
   float* stats_out;
 };
@@ -167,7 +175,7 @@ hipError_t launch_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_re
 
 hipError_t launch_compact_prepare(const Geo& g, const gp_pages& pg, const ScratchPtrs& sp,
                                   const uint8_t* decision, int32_t* evicted_out,
-                                  int32_t* status_out, hipStream_t st);
+                                  int32_t evicted_stride, int32_t* status_out, hipStream_t st);
 hipError_t launch_compact_move(const Geo& g, const gp_pages& pg, const ScratchPtrs& sp,
                                int32_t* counters_out, hipStream_t st);
 

@@ -276,8 +276,8 @@ hipError_t launch_logits(const ScanArgs& a, int64_t units, hipStream_t st) {
 hipError_t launch_scan(const Geo& g, const ScratchPtrs& sp, int64_t max_tokens,
                        const float* sum_s, const float* sum_l, const float* rope_cos,
                        const float* rope_sin, int32_t rope_max_pos, const int32_t* pos,
-                       float top_p, int32_t n_local, int32_t* ws_out, float* stats_out,
-                       hipStream_t st) {
+                       float top_p, int32_t n_local, int32_t shrink, int32_t* ws_out,
+                       float* stats_out, hipStream_t st) {
   ScanArgs a;
   a.g = g;
   a.sp = sp;
@@ -294,7 +294,7 @@ hipError_t launch_scan(const Geo& g, const ScratchPtrs& sp, int64_t max_tokens,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t units = (int64_t)g.n_req * g.L * g.Hkv;
-  FinishArgs f{g, sp, top_p, n_local, ws_out, stats_out};
+  FinishArgs f{g, sp, top_p, n_local, shrink, ws_out, stats_out};
   if (g.dtype == GP_BF16 && g.P % kFusedPageMultiple == 0) return launch_fused_scan(a, f, st);
   if (g.dtype == GP_BF16) {
     e = g.d == 128 ? launch_logits<true, 128>(a, units, st) : launch_logits<true, 64>(a, units, st);

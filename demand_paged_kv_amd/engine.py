@@ -57,7 +57,7 @@ class StepOutputs:
     decision: torch.Tensor    # [n] uint8
     delta: torch.Tensor       # [n] int32
     status: torch.Tensor      # [n] int32
-    evicted: torch.Tensor     # [n][L][Hkv][P] int32
+    evicted: torch.Tensor     # [n][L][Hkv][P] int32 ([..][2P] under the SHRINK policy)
     counters: torch.Tensor    # [GP_NUM_COUNTERS] int32
 
 
@@ -84,11 +84,19 @@ class BoundaryEngine:
             decision=torch.empty(n, dtype=torch.uint8, device=dev),
             delta=torch.empty(n, dtype=torch.int32, device=dev),
             status=torch.empty(n, dtype=torch.int32, device=dev),
-            evicted=torch.empty((n, st.L, st.Hkv, st.P), dtype=torch.int32, device=dev),
+            evicted=torch.empty(0, dtype=torch.int32, device=dev),
             counters=torch.zeros(B.GP_NUM_COUNTERS, dtype=torch.int32, device=dev),
         )
         self.max_batch = n
-        self.policy, self.rand_u, self.grow_prob = "growpage", None, 0.0
+        self._ev_store = torch.empty(n * st.L * st.Hkv * 2 * st.P, dtype=torch.int32, device=dev)
+        self.policy, self.rand_u, self.grow_prob = ("shrink" if prm.shrink else "growpage"), None, 0.0
+        self._view_evicted()
+
+    def _view_evicted(self):
+        """Evicted-slot rows are P wide, 2P under SHRINK (gp_compact's evicted_out)."""
+        st, n = self.st, self.max_batch
+        E = (2 if self.prm.shrink else 1) * st.P
+        self.out.evicted = self._ev_store[: n * st.L * st.Hkv * E].view(n, st.L, st.Hkv, E)
 
     def scan(self, req_ids: torch.Tensor, stream=None):
         st, o, nb = self.st, self.out, int(req_ids.numel())
@@ -115,6 +123,8 @@ class BoundaryEngine:
         assert policy in B.POLICIES
         assert policy != "random" or (rand_u is not None and rand_u.dtype == torch.float32)
         self.policy, self.rand_u, self.grow_prob = policy, rand_u, float(grow_prob)
+        self.prm.shrink = 1 if policy == "shrink" else 0  # the scan sizes keep-sets by it
+        self._view_evicted()
 
     def compact(self, req_ids: torch.Tensor, stream=None):
         o, nb = self.out, int(req_ids.numel())

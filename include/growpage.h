@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define GP_ABI_VERSION 1
+#define GP_ABI_VERSION 2
 
 typedef enum gp_status {
   GP_OK = 0,
@@ -70,6 +70,7 @@ typedef enum gp_dtype { GP_F32 = 0, GP_BF16 = 1 } gp_dtype;
 /* Decisions written to decision_out (device, uint8). */
 #define GP_DECISION_COMPACT 0
 #define GP_DECISION_GROW 1
+#define GP_DECISION_SHRINK 2   /* compacted into one allocation page fewer (GP_POLICY_SHRINK) */
 
 /* Counters written to counters_out (device, int32[GP_NUM_COUNTERS]).  gp_decide
  * writes GROWS and GROW_DENIED; gp_compact writes the others. */
@@ -82,7 +83,8 @@ enum {
   GP_CNT_FREED_PAGES = 5,    /* pages whose refcount reached 0 and were pushed      */
   GP_CNT_MOVED_ROWS = 6,     /* sum over compacted (layer, KV head) of rows moved   */
   GP_CNT_COPIED_ROWS = 7,    /* rows (per layer and KV head) copied by copy-on-write */
-  GP_NUM_COUNTERS = 8
+  GP_CNT_SHRINKS = 8,        /* requests that released an allocation page (SHRINK)   */
+  GP_NUM_COUNTERS = 9
 };
 
 /* Engine parameters (host struct, passed by pointer, read during the call only). */
@@ -92,6 +94,9 @@ typedef struct gp_params {
   float top_p;      /* working-set mass threshold; >= 1 means "all n slots"            */
   int32_t tau;      /* demand threshold: grow iff sum(W_S - W_L) > tau                 */
   int32_t n_local;  /* most recent slots always kept by a compaction (>= 0)            */
+  int32_t shrink;   /* 0, or 1 for the SHRINK policy: a compaction of a request holding
+                       A >= 2 allocation pages keeps (A-1)*P slots instead of A*P; must
+                       match the policy given to gp_decide_policy                      */
 } gp_params;
 
 /* Paged K/V pools (host struct).  Element (layer l, page p, KV head g, slot s, i) of
@@ -153,7 +158,9 @@ size_t gp_scratch_bytes(const gp_kv* kv, int32_t n_req, int64_t max_total_tokens
  * table rope_cos/rope_sin [rope_max_pos][d/2] float32 (both NULL = no rotation), scored
  * against all n = n_alloc*P + fill keys of the request (scale 1/sqrt(d)), and
  *   ws_out[b][l][h][s] = smallest m whose m largest softmax probabilities sum >= top_p
- * (s = 0 short, 1 long; top_p >= 1 gives n).  stats_out (optional, may be NULL):
+ * (s = 0 short, 1 long; top_p >= 1 gives n).  It also selects each (layer, KV head)'s
+ * evicted slots for a compaction into k = A*P slots (A = n_alloc; k = (A-1)*P when
+ * params->shrink and A >= 2).  stats_out (optional, may be NULL):
  * [n_req][L][Hq][2][2] float32 = (max logit, sum exp(logit - max)).  The logits and
  * statistics are also kept in `scratch` for gp_compact, so the same scratch must be
  * passed to gp_compact unchanged.  The page state is only read.
@@ -188,14 +195,21 @@ typedef enum {
   GP_POLICY_GROWPAGE = 0,        /* grow iff delta > tau (gp_decide)                         */
   GP_POLICY_RANDOM = 1,          /* grow iff rand_u[b] < grow_prob (frequency-matched random) */
   GP_POLICY_INVERSE = 2,         /* grow iff -delta > tau (signal direction reversed)        */
-  GP_POLICY_ALWAYS_COMPACT = 3   /* never grow (fixed per-request budget)                    */
+  GP_POLICY_ALWAYS_COMPACT = 3,  /* never grow (fixed per-request budget)                    */
+  GP_POLICY_SHRINK = 4           /* grow iff delta > tau; otherwise (also after a denied grow)
+                                    a request holding A >= 2 allocation pages is decided
+                                    SHRINK: compacted into (A-1)*P slots, its reference to
+                                    allocation page A-1 dropped and its write page moved to
+                                    page_table[r][A-1] (irreversible shrinking); requires
+                                    params->shrink == 1                                        */
 } gp_policy;
 
 /* gp_decide under a decision policy; everything but the grow/compact choice is as in
  * gp_decide (delta_out is always the signal).  rand_u: device float32 [n_req] uniform
  * draws in [0, 1), required for GP_POLICY_RANDOM and ignored otherwise; grow_prob: the
  * grow probability of GP_POLICY_RANDOM.  Errors: GP_ERR_INVALID for an unknown policy,
- * a missing rand_u, or the gp_decide conditions. */
+ * a missing rand_u, params->shrink not 1 exactly for GP_POLICY_SHRINK, or the gp_decide
+ * conditions (gp_decide itself requires params->shrink == 0). */
 gp_status gp_decide_policy(const int32_t* ws, const int32_t* req_ids, int32_t n_req, int32_t L,
                            int32_t Hq, int32_t P, const gp_params* params, int32_t policy,
                            const float* rand_u, float grow_prob, const gp_pages* pages,
@@ -204,15 +218,18 @@ gp_status gp_decide_policy(const int32_t* ws, const int32_t* req_ids, int32_t n_
 
 /* Compaction (GrowPage review, "Summary": compact within the current allocation by the
  * maximum of both temporal importance scores; abstract: prefix caching preserved).
- * For every batch entry with decision COMPACT and fill == P: selects the n - k evicted
- * slots of each (layer, KV head), copies-on-write the pages that would change and are
+ * For every batch entry with decision COMPACT or SHRINK and fill == P: takes the n - k
+ * evicted slots of each (layer, KV head) (k = A*P, or (A-1)*P for SHRINK, whose
+ * allocation page A-1 then loses this reference and whose write page moves to
+ * page_table[r][A-1], n_alloc = A-1), copies-on-write the pages that would change and are
  * shared (snapshot refcount > 1; fresh pages popped after gp_decide's grows, in batch
  * order and ascending page index), moves K and V rows in place, sets fill to 0,
  * decrements the refcounts of the replaced pages and pushes the pages that reach 0 in
  * ascending id order.  A request whose copy-on-write demand exceeds the free stack is
  * left untouched and flagged GP_REQ_DEFERRED (status_out is OR-ed, keep gp_decide's
- * bits).  evicted_out (optional): [n_req][L][Hkv][P] int32, ascending evicted slots,
- * -1 padded, for compacting entries.  Needs the scratch of the preceding
+ * bits).  evicted_out (optional): [n_req][L][Hkv][E] int32 with E = P (2P when
+ * params->shrink), ascending evicted slots, -1 padded, for compacting entries.
+ * params->shrink must be the value the scan used.  Needs the scratch of the preceding
  * gp_boundary_scan of the same batch, and gp_decide's decision_out. */
 gp_status gp_compact(const gp_kv* kv, const gp_pages* pages, const int32_t* req_ids,
                      const uint8_t* decision, int32_t n_req, const gp_params* params,

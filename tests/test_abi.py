@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gp_abi_version() == 1
+    assert lib.gp_abi_version() == 2
     for s in range(5):
         assert lib.gp_status_string(s).decode().startswith("GP_")
     assert b"unknown" in lib.gp_status_string(99)
@@ -96,6 +96,26 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert lib.gp_update_summaries(0x1000, 1, 4, 4, 6, 0x2000, 1, 2, 8, 64, 0x3000, 0x4000, P(prm), None) == B.GP_ERR_INVALID
     assert lib.gp_update_summaries(0x1000, 1, 4, 4, 4, 0x2000, 0, 2, 8, 64, 0x3000, 0x4000, P(prm), None) == B.GP_OK
     assert lib.gp_append_kv(P(kv), P(pg), None, 0x10, 0x9000, 1, None, None) == B.GP_ERR_INVALID
+    # SHRINK: the flag is 0 or 1, and the keep-sets the scan sized must match the policy
+    assert lib.gp_boundary_scan(*args(pr=B.params(shrink=2))) == B.GP_ERR_INVALID
+    sh = B.params(shrink=1)
+    assert lib.gp_decide(0x1, 0x9000, 1, 2, 32, 16, P(sh), P(pg), 1, 2, 3, None, None) == B.GP_ERR_INVALID
+    dp = lambda pr, pol: lib.gp_decide_policy(0x1, 0x9000, 0, 2, 32, 16, P(pr), pol, None, 0.0, P(pg),
+                                              1, 2, 3, None, None)
+    assert dp(sh, B.POLICIES["shrink"]) == B.GP_OK                   # empty batch: nothing launched
+    assert dp(prm, B.POLICIES["shrink"]) == B.GP_ERR_INVALID
+    assert dp(sh, B.POLICIES["growpage"]) == B.GP_ERR_INVALID
+    assert dp(prm, 5) == B.GP_ERR_INVALID
+
+
+def test_param_struct_matches_header():
+    """The binding's gp_params mirror has the header's fields in the header's order."""
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct gp_params \{(.*?)\} gp_params;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"(?:float|int32_t)\s+([\w\s,]+);", body)
+    names = [n.strip() for f in fields for n in f.split(",")]
+    assert names == [f[0] for f in B.Params._fields_]
 
 
 def test_single_hip_runtime_after_load():

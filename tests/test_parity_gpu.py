@@ -205,7 +205,7 @@ def test_planted_logits(name, fns, params):
     _say(name, rep, res.counters, "W", res.W[:, 0, 0].tolist())
 
 
-@pytest.mark.parametrize("policy", ["growpage", "random", "inverse", "always_compact"])
+@pytest.mark.parametrize("policy", ["growpage", "random", "inverse", "always_compact", "shrink"])
 def test_decision_policies(policy):
     """The ablation policies through gp_decide_policy, the rest of the batch as usual."""
     from demand_paged_kv_amd import binding as Bd
@@ -223,3 +223,40 @@ def test_decision_policies(policy):
     out = eng.step(torch.arange(wl.B, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     compare_step(wl, np.arange(wl.B), st, out, res, wl.params["n_local"])
+
+
+SHRINK_CASES = [
+    # shared prefixes: copy-on-write below the released page, shared released pages
+    ("shrink_cow_p16", dict(B=8, L=2, Hq=32, Hkv=8, d=128, P=16, ctx=(40, 600), grow_frac=0.3, prefix_groups=2,
+                            prefix_pages=3, spare_pages=40, params=dict(SW.PARAMS_DEFAULT, n_local=16))),
+    # 2P = 512 evicted slots per unit, the pages' operating point
+    ("shrink_p256", dict(B=4, L=1, Hq=32, Hkv=8, d=128, P=256, ctx=(300, 2500), grow_frac=0.3,
+                         params=dict(SW.PARAMS_DEFAULT, top_p=0.99, n_local=64))),
+    # float32 keys, page 8 (the vector-unit scan), one-page allocations that compact in place
+    ("shrink_f32_p8", dict(B=8, L=2, Hq=8, Hkv=2, d=64, P=8, dtype="f32", ctx=(4, 200), grow_frac=0.3,
+                           params=dict(SW.PARAMS_DEFAULT, n_local=4))),
+]
+
+
+@pytest.mark.parametrize("name,kw", SHRINK_CASES, ids=[c[0] for c in SHRINK_CASES])
+def test_shrink_policy(name, kw):
+    """GP_POLICY_SHRINK end to end against the oracle's SHRINK step: keep-sets of (A-1)P
+    slots, released pages, write pages moved, pool state and page contents."""
+    from demand_paged_kv_amd import binding as Bd
+    from demand_paged_kv_amd.engine import BoundaryEngine
+    from synth import device as SD
+    wl = SW.direct_case(seed=zlib.crc32(name.encode()) % 10000, name=name, **kw)
+    prm = dict(wl.params, policy="shrink")
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, prm)
+    _say(f"[shrink] {name}: A {wl.n_alloc.tolist()} decisions {res.decision.tolist()} counters {res.counters}")
+    assert res.counters["shrinks"] > 0
+    st = SD.upload(wl, "cuda")
+    eng = BoundaryEngine(st, wl.B, wl.total_tokens(), Bd.params_from(prm))
+    assert eng.policy == "shrink" and eng.out.evicted.shape[-1] == 2 * wl.P
+    out = eng.step(torch.arange(wl.B, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    rep = compare_step(wl, np.arange(wl.B), st, out, res, wl.params["n_local"])
+    c = dict(zip(Bd.COUNTER_NAMES, out.counters.cpu().numpy().tolist()))
+    for key in ("shrinks", "compacts", "deferred", "cow_pages", "freed_pages"):
+        assert c[key] == res.counters[key], (key, c[key], res.counters[key])
+    _say(name, rep)
