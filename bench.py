@@ -61,6 +61,10 @@ def parse():
                          "correlation with the later working set) or overlap (decode attention with the "
                          "boundary engine serial vs on a second stream), each reported on its own line")
     ap.add_argument("--decode-steps", type=int, default=4096)
+    ap.add_argument("--ordinary-pools", action="store_true",
+                    help="allocate the K/V pools in ordinary device memory instead of asking for "
+                         "physically contiguous memory (the compaction's row moves vary with the "
+                         "physical pages behind ordinary allocations)")
     ap.add_argument("--schedules", default="serial,overlap",
                     help="overlap workload: schedules to run (serial, overlap)")
     ap.add_argument("--paper", action="store_true",
@@ -118,9 +122,9 @@ def main():
     if args.paper:
         from synth import workloads as SW
         gw = GW.boundary_sweep(seed=args.seed + 100, P=256, num_pages=1536, params=dict(SW.PARAMS_PAPER),
-                               name="boundary_sweep_paper")
+                               name="boundary_sweep_paper", contiguous=not args.ordinary_pools)
     else:
-        gw = GW.boundary_sweep(seed=args.seed)
+        gw = GW.boundary_sweep(seed=args.seed, contiguous=not args.ordinary_pools)
     st = gw.st
     torch.cuda.synchronize()
     log(f"workload generated in {time.time() - t0:.1f}s: {gw.B} requests, {gw.total_tokens()} tokens, "
@@ -212,7 +216,8 @@ def main():
                                 "broadening, 1536-page pool"),
                    "requests": gw.B, "layers": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "page_size": P, "tokens": sum_n, "pool_pages": st.num_pages, "top_p": gw.params["top_p"],
-                   "n_local": gw.params["n_local"], "seed": gw.seed, "storage_dtype": "bf16"},
+                   "n_local": gw.params["n_local"], "seed": gw.seed, "storage_dtype": "bf16",
+                   "pool_memory": gw.pool_memory},
         "tokens_scanned_per_s": round(L * sum_n / step_s, 1),
         "algorithmic_GBps": round(alg_bytes / step_s / 1e9, 1),
         "hbm_frac": round(alg_bytes / step_s / 1e9 / HBM_PEAK_GBPS, 4),
@@ -242,7 +247,7 @@ def decode_loop(args):
 
     Bd.load()
     spec = DecodeSpec(steps=args.decode_steps)
-    gen = DecodeLoopGen(spec, "cuda")
+    gen = DecodeLoopGen(spec, "cuda", contiguous=not args.ordinary_pools)
     st = gen.initial_state()
     torch.cuda.synchronize()
     eng = BoundaryEngine(st, spec.B, spec.B * (spec.prompt + spec.steps + spec.P), Bd.params_from(spec.params))
@@ -314,7 +319,8 @@ def decode_loop(args):
                                f"1024-token prompts, {spec.steps} decode steps, boundary every 16 steps",
                    "requests": spec.B, "layers": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "page_size": spec.P, "prompt": spec.prompt, "pool_pages": spec.num_pages,
-                   "top_p": spec.params["top_p"], "n_local": spec.params["n_local"], "seed": spec.seed},
+                   "top_p": spec.params["top_p"], "n_local": spec.params["n_local"], "seed": spec.seed,
+                   "pool_memory": gen.pool_memory},
         "boundary_batches": n_bound,
         "scans": n_bound * spec.B,
         "tokens_scanned_per_s": round(L * scanned / s_all, 1),
@@ -355,7 +361,7 @@ def policies(args):
     sig = None
     for policy in ("growpage", "random", "inverse", "always_compact", "shrink"):
         spec = DecodeSpec(steps=steps)
-        gen = DecodeLoopGen(spec, "cuda")
+        gen = DecodeLoopGen(spec, "cuda", contiguous=not args.ordinary_pools)
         st = gen.initial_state()
         eng = BoundaryEngine(st, spec.B, spec.B * (spec.prompt + spec.steps + spec.P),
                              Bd.params_from(dict(spec.params, policy=policy)))
@@ -435,7 +441,7 @@ def overlap(args):
     res = {}
     for mode in args.schedules.split(","):
         spec = DecodeSpec(steps=steps + warm, stagger=True)
-        gen = DecodeLoopGen(spec, "cuda")
+        gen = DecodeLoopGen(spec, "cuda", contiguous=not args.ordinary_pools)
         st = gen.initial_state()
         eng = BoundaryEngine(st, spec.B, spec.B * (spec.prompt + spec.steps + 2 * spec.P),
                              Bd.params_from(spec.params))
@@ -539,7 +545,7 @@ def prefix_share(args):
 
     Bd.load()
     t0 = time.time()
-    gw = GW.prefix_share(seed=5000)
+    gw = GW.prefix_share(seed=5000, contiguous=not args.ordinary_pools)
     st = gw.st
     torch.cuda.synchronize()
     log(f"workload generated in {time.time() - t0:.1f}s: {gw.B} requests, {gw.total_tokens()} tokens, "
@@ -576,7 +582,7 @@ def prefix_share(args):
                                "groups of 16 sharing a 2048-token prefix, contexts log-uniform 1024-32768, "
                                "pool 80% of full-KV demand",
                    "requests": gw.B, "layers": L, "page_size": st.P, "tokens": sum_n,
-                   "pool_pages": st.num_pages, "seed": gw.seed},
+                   "pool_pages": st.num_pages, "seed": gw.seed, "pool_memory": gw.pool_memory},
         "tokens_scanned_per_s": round(L * sum_n / s_, 1),
         "algorithmic_GBps": round(alg / s_ / 1e9, 1),
         "hbm_frac": round(alg / s_ / 1e9 / HBM_PEAK_GBPS, 4),

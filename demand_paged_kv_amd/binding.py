@@ -25,7 +25,8 @@ GP_NUM_COUNTERS = len(COUNTER_NAMES)
 EXPORTED = ("gp_abi_version", "gp_status_string", "gp_last_hip_error_string", "gp_update_summaries",
             "gp_scratch_bytes",
             "gp_boundary_scan", "gp_decide", "gp_decide_policy", "gp_compact", "gp_compact_prepare",
-            "gp_compact_move", "gp_append_kv", "gp_decode_attention")
+            "gp_compact_move", "gp_append_kv", "gp_decode_attention", "gp_contiguous_malloc",
+            "gp_contiguous_free")
 # decision policies (gp_decide_policy)
 POLICIES = {"growpage": 0, "random": 1, "inverse": 2, "always_compact": 3, "shrink": 4}
 
@@ -103,6 +104,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                         i32, P, P, i32, P, P, P]
     lib.gp_append_kv.restype = i32
     lib.gp_append_kv.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Pages), P, P, P, i32, P, P]
+    lib.gp_contiguous_malloc.restype = P
+    lib.gp_contiguous_malloc.argtypes = [i64, i32, P]
+    lib.gp_contiguous_free.restype = None
+    lib.gp_contiguous_free.argtypes = [P, i64, i32, P]
     _lib = lib
     return lib
 

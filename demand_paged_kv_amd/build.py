@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libgrowpage.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "ema.hip", "scan.hip", "finish.hip", "decide.hip", "compact.hip", "attn.hip"]
+SOURCES = ["api.hip", "ema.hip", "scan.hip", "finish.hip", "decide.hip", "compact.hip", "attn.hip",
+           "pool_alloc.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

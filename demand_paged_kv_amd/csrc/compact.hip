@@ -15,7 +15,7 @@
 //   cowassign_kernel per entry: assign popped pages in ascending page index, rewrite the
 //                    page table, record (old, new).
 //   cowcopy_kernel   copy every (old page, layer, KV head) block of K and V to the new page.
-//   gather_kernel    per unit and tensor (K blocks first, then V blocks): in-place stable
+//   gather_kernel    per unit and tensor (K and V blocks of a unit adjacent): in-place stable
 //                    compaction, slot j <- slot kept[j] for j in [e, k), 128 destination
 //                    rows per step, all reads of a step before its writes (destinations
 //                    never exceed sources).
@@ -254,10 +254,11 @@ __device__ __forceinline__ int shift_of(const int* thr, int E, int j) {
   return lo;
 }
 
-// One block moves the rows of one tensor (K or V) of one unit; all K blocks come before
-// all V blocks in the grid, so the two tensors are never walked in lockstep (identical
-// in-pool offsets of K and V would otherwise hit the same HBM channels together).  A
-// step moves 128 destination rows; in each of its load/store instructions the 256
+// One block moves the rows of one tensor (K or V) of one unit; a unit's K and V blocks
+// are adjacent in the grid, so both pools are walked together (on physically contiguous
+// pools this measured 7.4 ms against 8.3 ms for all K blocks before all V blocks on the
+// 32-layer sweep; on scattered pools the two orders tie).  A step moves 128 destination
+// rows; in each of its load/store instructions the 256
 // threads cover 256/CPR whole rows contiguously (lane t takes 16-byte piece t % CPR of a
 // row), so every store writes complete cache lines.
 template <int CPR>  // 16-byte pieces per row
@@ -269,10 +270,9 @@ __global__ __launch_bounds__(256) void gather_kernel(CompactArgs a) {
   __shared__ int s_thr[2 * 256];  // E <= 2P <= 512
   __shared__ int s_pt[kPtLds];
   const int tid = threadIdx.x;
-  const int units = g.n_req * g.L * g.Hkv;
-  const int which = blockIdx.x >= units ? 1 : 0;
+  const int which = blockIdx.x & 1;
   int b, l, kvh;
-  unit_of_block(g, a.sp, blockIdx.x - which * units, b, l, kvh);
+  unit_of_block(g, a.sp, blockIdx.x >> 1, b, l, kvh);
   const int32_t* rq = a.sp.req + (int64_t)b * RQ_N;
   if (rq[RQ_STATE] != ST_GO) return;
   const int r = g.req_ids[b];
@@ -462,7 +462,7 @@ hipError_t launch_compact_move(const Geo& g, const gp_pages& pg, const ScratchPt
   const unsigned units = (unsigned)((int64_t)g.n_req * g.L * g.Hkv);
   const int esz = g.dtype == GP_BF16 ? 2 : 4;
   const int cpr = g.d * esz / 16;  // 16-byte pieces per row: 8, 16 or 32
-  const dim3 grid(2 * units);      // K blocks, then V blocks
+  const dim3 grid(2 * units);      // K and V block of each unit, adjacent
   if (cpr == 8)
     hipLaunchKernelGGL(gather_kernel<8>, grid, dim3(256), 0, st, a);
   else if (cpr == 16)

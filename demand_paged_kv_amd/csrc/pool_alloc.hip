@@ -1,0 +1,36 @@
+// Physically contiguous device memory for the K/V pools (a deployment helper, not part of
+// the boundary path).  The boundary kernels address pool pages at random; on MI355X the
+// row moves of a compaction ran in 7.4-7.5 ms on contiguous pools in every trial, while
+// ordinary allocations gave 7.5, 8.4 or 9.1 ms depending on the physical pages behind
+// them.  The two functions have the signatures of a PyTorch pluggable allocator.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "growpage.h"
+
+extern "C" {
+
+void* gp_contiguous_malloc(int64_t size, int32_t device, void* stream) {
+  (void)stream;
+  if (size <= 0) return nullptr;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != device && hipSetDevice(device) != hipSuccess) return nullptr;
+  void* p = nullptr;
+  if (hipExtMallocWithFlags(&p, (size_t)size, hipDeviceMallocContiguous) != hipSuccess) p = nullptr;
+  if (cur != device) (void)hipSetDevice(cur);
+  return p;
+}
+
+void gp_contiguous_free(void* ptr, int64_t size, int32_t device, void* stream) {
+  (void)size;
+  (void)stream;
+  if (!ptr) return;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return;
+  if (cur != device) (void)hipSetDevice(device);
+  (void)hipFree(ptr);
+  if (cur != device) (void)hipSetDevice(cur);
+}
+
+}  // extern "C"

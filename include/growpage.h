@@ -250,6 +250,15 @@ gp_status gp_compact_move(const gp_kv* kv, const gp_pages* pages, const int32_t*
                           int32_t n_req, int32_t* counters_out, void* scratch,
                           size_t scratch_bytes, int64_t max_total_tokens, void* stream);
 
+/* Deployment helper (not part of the boundary path): physically contiguous device memory
+ * for the K/V pools, with the signatures of a PyTorch pluggable allocator
+ * (torch.cuda.memory.CUDAPluggableAllocator).  The compaction's row moves address pool
+ * pages at random and measured fastest, and repeatable, on contiguous pools.  Returns
+ * NULL when the device cannot supply `size` contiguous bytes; the caller then allocates
+ * ordinary memory.  The stream argument is unused. */
+void* gp_contiguous_malloc(int64_t size, int32_t device, void* stream);
+void gp_contiguous_free(void* ptr, int64_t size, int32_t device, void* stream);
+
 /* Decode-loop helper: append one token per batch entry.  k_new, v_new:
  * [n_req][L][Hkv][d] of kv->dtype (contiguous).  Writes slot fill[r] of the write page
  * page_table[r][n_alloc[r]] and increments fill[r]; entries already at fill == P are

@@ -23,6 +23,7 @@ import numpy as np
 import torch
 
 from demand_paged_kv_amd import binding as Bd
+from demand_paged_kv_amd import pool as PM
 from demand_paged_kv_amd.engine import DeviceState
 
 from . import workloads as SW
@@ -87,9 +88,11 @@ def _phase_table(rng, spec: DecodeSpec) -> np.ndarray:
 class DecodeLoopGen:
     """Builds the initial device state and yields each step's queries and K/V rows."""
 
-    def __init__(self, spec: DecodeSpec, device="cuda"):
+    def __init__(self, spec: DecodeSpec, device="cuda", contiguous: bool = False):
         self.spec = spec
         self.device = device
+        self.contiguous = contiguous   # K/V pools in physically contiguous memory if available
+        self.pool_memory = "ordinary"
         rng = np.random.default_rng(spec.seed)
         self.gen = torch.Generator(device=device)
         self.gen.manual_seed(spec.seed)
@@ -125,8 +128,12 @@ class DecodeLoopGen:
         free = self.perm[used:]
         stack = np.zeros(sp.num_pages, np.int32)
         stack[: len(free)] = free
-        k_pool = torch.zeros((sp.L, sp.num_pages, sp.Hkv, P, sp.d), dtype=torch.bfloat16, device=dev)
-        v_pool = torch.zeros_like(k_pool)
+        shape = (sp.L, sp.num_pages, sp.Hkv, P, sp.d)
+        k_pool, kk = PM.empty(shape, torch.bfloat16, dev, self.contiguous)
+        v_pool, vk = PM.empty(shape, torch.bfloat16, dev, self.contiguous)
+        k_pool.zero_()
+        v_pool.zero_()
+        self.pool_memory = "contiguous" if kk == vk == "contiguous" else "ordinary"
         npg = A0 + 1 if sp.stagger else A0                                         # pages holding prompt rows
         pages = torch.from_numpy(table[:, :npg].astype(np.int64)).to(dev)          # [B][npg]
         T = npg * P

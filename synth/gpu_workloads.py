@@ -19,6 +19,7 @@ import numpy as np
 import torch
 
 from demand_paged_kv_amd import binding as Bd
+from demand_paged_kv_amd import pool as PM
 from demand_paged_kv_amd.engine import DeviceState
 
 from . import workloads as SW
@@ -34,6 +35,7 @@ class GpuWorkload:
     params: dict
     seed: int
     name: str
+    pool_memory: str = "ordinary"   # "contiguous": K/V pools in physically contiguous memory
 
     @property
     def B(self):
@@ -49,22 +51,25 @@ def _rotate(u: torch.Tensor, c: torch.Tensor, s: torch.Tensor) -> torch.Tensor:
     return torch.cat([x1 * c - x2 * s, x2 * c + x1 * s], dim=-1)
 
 
-def pool_pair(L, num_pages, Hkv, P, d, layout, device):
+def pool_pair(L, num_pages, Hkv, P, d, layout, device, contiguous=False):
     """K and V pools as [L][num_pages][Hkv][P][d] views: "layer_major" stores them in that
-    order; "page_major" stores [num_pages][L][Hkv][P][d] (all layers of a page together)."""
-    if layout == "layer_major":
-        k = torch.empty((L, num_pages, Hkv, P, d), dtype=torch.bfloat16, device=device)
-        return k, torch.empty_like(k)
-    assert layout == "page_major", layout
-    k = torch.empty((num_pages, L, Hkv, P, d), dtype=torch.bfloat16, device=device).permute(1, 0, 2, 3, 4)
-    v = torch.empty((num_pages, L, Hkv, P, d), dtype=torch.bfloat16, device=device).permute(1, 0, 2, 3, 4)
-    return k, v
+    order; "page_major" stores [num_pages][L][Hkv][P][d] (all layers of a page together).
+    With ``contiguous`` each pool is asked for physically contiguous memory.  Returns
+    (k, v, kind) with kind "contiguous" when both pools got it."""
+    shape = (L, num_pages, Hkv, P, d) if layout == "layer_major" else (num_pages, L, Hkv, P, d)
+    assert layout in ("layer_major", "page_major"), layout
+    k, kk = PM.empty(shape, torch.bfloat16, device, contiguous)
+    v, vk = PM.empty(shape, torch.bfloat16, device, contiguous)
+    if layout == "page_major":
+        k, v = k.permute(1, 0, 2, 3, 4), v.permute(1, 0, 2, 3, 4)
+    return k, v, ("contiguous" if kk == vk == "contiguous" else "ordinary")
 
 
 def boundary_sweep(seed: int = 3000, B: int = 64, L: int = 32, Hq: int = 32, Hkv: int = 8, d: int = 128,
                    P: int = 16, num_pages: int = 24576, ctx=(512, 16384), grow_frac: float = 0.3,
                    s_zipf: float = 1.1, params: dict | None = None, device="cuda",
-                   name: str = "boundary_sweep", layout: str = "layer_major") -> GpuWorkload:
+                   name: str = "boundary_sweep", layout: str = "layer_major",
+                   contiguous: bool = False) -> GpuWorkload:
     rng = np.random.default_rng(seed)
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
@@ -101,7 +106,7 @@ def boundary_sweep(seed: int = 3000, B: int = 64, L: int = 32, Hq: int = 32, Hkv
     sum_s = (bs[..., None] * u + 0.1 * torch.randn((B, L, Hq, d), generator=gen, device=device, dtype=torch.float64)).float()
     sum_l = (bl[..., None] * u + 0.1 * torch.randn((B, L, Hq, d), generator=gen, device=device, dtype=torch.float64)).float()
 
-    k_pool, v_pool = pool_pair(L, num_pages, Hkv, P, d, layout, device)
+    k_pool, v_pool, mem = pool_pair(L, num_pages, Hkv, P, d, layout, device, contiguous)
     for l in range(L):           # V and unused K pages: N(0, 1)
         k_pool[l].normal_(generator=gen)
         v_pool[l].normal_(generator=gen)
@@ -127,14 +132,14 @@ def boundary_sweep(seed: int = 3000, B: int = 64, L: int = 32, Hq: int = 32, Hkv
                      free_top=torch.tensor([len(free)], dtype=torch.int32, device=device),
                      sum_s=sum_s.contiguous(), sum_l=sum_l.contiguous(),
                      pos=torch.from_numpy(pos.astype(np.int32)).to(device), rope_cos=cos, rope_sin=sin)
-    return GpuWorkload(st, n, A, regime, pos, dict(params or SW.PARAMS_DEFAULT), seed, name)
+    return GpuWorkload(st, n, A, regime, pos, dict(params or SW.PARAMS_DEFAULT), seed, name, mem)
 
 
 def prefix_share(seed: int = 5000, B: int = 256, L: int = 36, Hq: int = 32, Hkv: int = 8, d: int = 128,
                  P: int = 32, ctx=(1024, 32768), group: int = 16, prefix_pages: int = 64,
                  pool_frac: float = 0.8, alloc_frac: float = 0.8, grow_frac: float = 0.3, s_range=(0.8, 1.6),
                  free_pages: int | None = None, params: dict | None = None, device="cuda",
-                 name: str = "prefix_share") -> GpuWorkload:
+                 name: str = "prefix_share", contiguous: bool = False) -> GpuWorkload:
     """Prefix-sharing stress: groups of ``group`` consecutive requests share their first
     ``prefix_pages`` pages (refcount = group), contexts log-uniform in ``ctx``, Zipf
     exponent per request uniform in ``s_range``.  The pool holds ``pool_frac`` of the
@@ -196,8 +201,7 @@ def prefix_share(seed: int = 5000, B: int = 256, L: int = 36, Hq: int = 32, Hkv:
     sum_s = (bs[..., None] * ug + 0.1 * torch.randn((B, L, Hq, d), generator=gen, device=device, dtype=torch.float64)).float()
     sum_l = (bl[..., None] * ug + 0.1 * torch.randn((B, L, Hq, d), generator=gen, device=device, dtype=torch.float64)).float()
 
-    k_pool = torch.empty((L, num_pages, Hkv, P, d), dtype=torch.bfloat16, device=device)
-    v_pool = torch.empty_like(k_pool)
+    k_pool, v_pool, mem = pool_pair(L, num_pages, Hkv, P, d, "layer_major", device, contiguous)
     for l in range(L):
         k_pool[l].normal_(generator=gen)
         v_pool[l].normal_(generator=gen)
@@ -231,7 +235,7 @@ def prefix_share(seed: int = 5000, B: int = 256, L: int = 36, Hq: int = 32, Hkv:
                      free_top=torch.tensor([len(free)], dtype=torch.int32, device=device),
                      sum_s=sum_s.contiguous(), sum_l=sum_l.contiguous(),
                      pos=torch.from_numpy(pos.astype(np.int32)).to(device), rope_cos=cos, rope_sin=sin)
-    return GpuWorkload(st, n, A, regime, pos, dict(params or SW.PARAMS_DEFAULT), seed, name)
+    return GpuWorkload(st, n, A, regime, pos, dict(params or SW.PARAMS_DEFAULT), seed, name, mem)
 
 
 class StateBackup:

@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "growpage.h")
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:gp_status|int32_t|size_t|const char\*)\s+(gp_\w+)\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:gp_status|int32_t|size_t|const char\*|void\*|void)\s+(gp_\w+)\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")

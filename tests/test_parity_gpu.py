@@ -260,3 +260,35 @@ def test_shrink_policy(name, kw):
     for key in ("shrinks", "compacts", "deferred", "cow_pages", "freed_pages"):
         assert c[key] == res.counters[key], (key, c[key], res.counters[key])
     _say(name, rep)
+
+
+def test_contiguous_pools():
+    """Pools in the library's physically contiguous memory (gp_contiguous_malloc through
+    torch's pluggable allocator): the allocation is served, and a boundary step on those
+    pools matches the oracle like any other memory."""
+    from demand_paged_kv_amd import binding as Bd
+    from demand_paged_kv_amd import pool as PM
+    from demand_paged_kv_amd.engine import BoundaryEngine
+    from synth import device as SD
+    t, kind = PM.empty((3, 1 << 20), torch.float32, "cuda")
+    assert kind == "contiguous" and t.data_ptr() % 4096 == 0
+    t.copy_(torch.arange(3 << 20, dtype=torch.float32, device="cuda").view(3, 1 << 20))
+    assert float(t[2, 5].item()) == float((2 << 20) + 5)
+    del t
+    name = "contiguous_pools"
+    wl = SW.direct_case(seed=zlib.crc32(name.encode()) % 10000, B=6, L=2, Hq=32, Hkv=8, d=128, P=16,
+                        ctx=(100, 1500), grow_frac=0.4, prefix_groups=2, prefix_pages=2, spare_pages=30,
+                        name=name)
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, wl.params)
+    st = SD.upload(wl, "cuda")
+    for f in ("k_pool", "v_pool"):
+        src = getattr(st, f)
+        dst, kind = PM.empty(src.shape, src.dtype, "cuda")
+        assert kind == "contiguous"
+        dst.copy_(src)
+        setattr(st, f, dst)
+    eng = BoundaryEngine(st, wl.B, wl.total_tokens(), Bd.params_from(wl.params))
+    out = eng.step(torch.arange(wl.B, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    rep = compare_step(wl, np.arange(wl.B), st, out, res, wl.params["n_local"])
+    _say(name, rep, res.counters)
