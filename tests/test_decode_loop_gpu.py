@@ -50,9 +50,11 @@ def _gpu_step(eng, st, spec, t, q, k, v, fill, req):
     return bids, out
 
 
-def test_decode_loop_end_to_end_reduced():
+@pytest.mark.parametrize("policy", ["growpage", "shrink"])
+def test_decode_loop_end_to_end_reduced(policy):
     from synth.decode_loop import DecodeLoopGen, DecodeSpec
     spec = DecodeSpec(B=4, L=4, steps=512, seed=4000)
+    spec.params = dict(spec.params, policy=policy)
     gen = DecodeLoopGen(spec, "cuda")
     st = gen.initial_state()
     ost = DU.oracle_state(st, np.arange(spec.B))
@@ -85,10 +87,13 @@ def test_decode_loop_end_to_end_reduced():
         if boundaries % 8 == 0:
             _say(f"[decode] step {t}: {boundaries} boundaries, {compared} compared")
     dec = np.concatenate(decisions)
-    _say(f"[decode] {boundaries} boundaries, {compared} compared, grows {int(dec.sum())} of {dec.size}")
+    grows = int((dec == 1).sum())
+    _say(f"[decode] {policy}: {boundaries} boundaries, {compared} compared, grows {grows} of {dec.size}")
     assert boundaries == spec.steps // spec.P
     assert compared >= boundaries // 2
-    assert 0 < dec.sum() < dec.size, "both decisions should occur"
+    assert 0 < grows < dec.size, "both decisions should occur"
+    if policy == "shrink":
+        assert (dec == 2).any() and int(st.n_alloc[: spec.B].min().item()) < spec.A0
 
 
 def test_decode_loop_full_shape_sampled():

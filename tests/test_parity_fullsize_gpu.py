@@ -63,3 +63,34 @@ def test_paper_operating_point_full_size_sampled():
     dec = out.decision.cpu().numpy()
     check_pool(st, before, dec, np.arange(gw.B))
     print("[paper]", rep, "grows", int(dec.sum()), flush=True)
+
+
+def test_boundary_sweep_full_size_shrink():
+    """The benchmark batch under the SHRINK policy: sampled requests against the oracle's
+    SHRINK step, the whole batch's page state replayed from the GPU's own decisions."""
+    from demand_paged_kv_amd import binding as Bd
+    from demand_paged_kv_amd.engine import BoundaryEngine
+    from synth import gpu_workloads as GW
+    from tests.parity_util import check_pool_shared
+
+    gw = GW.boundary_sweep(seed=3000)
+    st = gw.st
+    params = dict(gw.params, policy="shrink")
+    order = np.argsort(-gw.n)
+    sample = sorted({int(order[0]), int(order[-1]), int(np.flatnonzero(gw.regime == 1)[0]),
+                     int(np.flatnonzero(gw.regime == 0)[0]), int(np.flatnonzero(gw.regime == 0)[-1])})
+    wl = GW.to_host_workload(gw, sample)
+    before = snapshot(st)
+    eng = BoundaryEngine(st, gw.B, gw.total_tokens(), Bd.params_from(params))
+    out = eng.step(torch.arange(gw.B, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    print("[fullsize-shrink] step done; oracle on sample", sample, flush=True)
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, params)
+    rep = compare_requests(wl, sample, st, out, res, gw.params["n_local"])
+    summary = check_pool_shared(st, before, out, gw.B, st.P, int(gw.params["tau"]), shrink=True)
+    dec = out.decision.cpu().numpy()[: gw.B]
+    assert np.array_equal(dec == 1, gw.regime == 1), (dec, gw.regime)
+    assert np.all(dec[gw.regime == 0] == 2)
+    c = dict(zip(Bd.COUNTER_NAMES, out.counters.cpu().numpy().tolist()))
+    assert c["shrinks"] == int((gw.regime == 0).sum()) == summary["freed"]
+    print("[fullsize-shrink]", rep, c, flush=True)
