@@ -1,8 +1,9 @@
 // Physically contiguous device memory for the K/V pools (a deployment helper, not part of
-// the boundary path).  The boundary kernels address pool pages at random; on MI355X the
-// row moves of a compaction ran in 7.4-7.5 ms on contiguous pools in every trial, while
-// ordinary allocations gave 7.5, 8.4 or 9.1 ms depending on the physical pages behind
-// them.  The two functions have the signatures of a PyTorch pluggable allocator.
+// the boundary path).  The boundary kernels address pool pages at random, and the row
+// moves of a compaction run at one of a few speeds set by the physical pages behind the
+// pools; on MI355X contiguous pools landed in the fast one somewhat more often than
+// ordinary allocations.  The two functions have the signatures of a PyTorch pluggable
+// allocator.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -1,7 +1,8 @@
 """Physically contiguous device memory for K/V pools, from the library's
 gp_contiguous_malloc / gp_contiguous_free.  Allocation plumbing only: the compaction's
-row moves address pool pages at random and ran fastest, and repeatably, on contiguous
-pools; the kernels themselves work on any device memory.
+row moves address pool pages at random, and their speed depends on the physical pages
+behind the pools (contiguous pools were fast somewhat more often); the kernels
+themselves work on any device memory.
 
 The memory is handed to torch through the CUDA array interface, so torch's own caching
 allocator never sees it: the returned tensor keeps the owning object alive, and the
