@@ -187,3 +187,41 @@ class BoundaryEngine:
         if boundary_ids is None or boundary_ids.numel() == 0:
             return None
         return self.step(boundary_ids, stream)
+
+
+class DecodeGraph:
+    """A decode step of an engine as HIP graphs, replayed with one launch each: ``plain``
+    (summaries absorb q, the K/V row is appended) and ``boundary`` (the same, then one
+    boundary batch over the requests in ``bids``).  Inputs are read from the static
+    buffers ``q``, ``k``, ``v`` and ``bids`` that the caller fills before each replay;
+    outputs land in the engine's buffers exactly as with eager calls.  The captured
+    kernels allocate nothing and synchronize nothing; capturing runs no kernel, so the
+    state is untouched until the first replay."""
+
+    def __init__(self, eng: "BoundaryEngine", req_ids: torch.Tensor, n_boundary: int,
+                 q_dtype=torch.bfloat16):
+        st = eng.st
+        dev = st.k_pool.device
+        n = int(req_ids.numel())
+        assert 0 < n_boundary <= eng.max_batch
+        kv_dtype = torch.bfloat16 if st.dtype == B.GP_BF16 else torch.float32
+        self.eng, self.req = eng, req_ids
+        self.q = torch.zeros((n, st.L, st.Hq, st.d), dtype=q_dtype, device=dev)
+        self.k = torch.zeros((n, st.L, st.Hkv, st.d), dtype=kv_dtype, device=dev)
+        self.v = torch.zeros_like(self.k)
+        self.bids = torch.zeros(n_boundary, dtype=torch.int32, device=dev)
+        self.plain = torch.cuda.CUDAGraph()
+        self.boundary = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.plain):
+            eng.update_summaries(self.q, req_ids)
+            eng.append(self.k, self.v, req_ids)
+        with torch.cuda.graph(self.boundary):
+            eng.update_summaries(self.q, req_ids)
+            eng.append(self.k, self.v, req_ids)
+            eng.step(self.bids)
+
+    def replay(self, boundary: bool) -> Optional[StepOutputs]:
+        """One decode step from the static buffers; returns the engine's outputs after a
+        boundary batch, None otherwise."""
+        (self.boundary if boundary else self.plain).replay()
+        return self.eng.out if boundary else None

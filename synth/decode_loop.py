@@ -161,10 +161,11 @@ class DecodeLoopGen:
             pos=torch.from_numpy((sp.prompt + self.fill0).astype(np.int32)).to(dev),
             rope_cos=self.cos, rope_sin=self.sin)
 
-    def step(self):
+    def step(self, out=None):
         """Inputs of the next decode step: q [B][L][Hq][d], k, v [B][L][Hkv][d] (bf16).
         Request r's token (and query) of step t sit at absolute position
-        prompt + fill0[r] + t."""
+        prompt + fill0[r] + t.  With ``out`` = (q, k, v) bf16 buffers the step is written
+        into them (and they are returned)."""
         sp = self.spec
         t = self.t
         assert t < sp.steps
@@ -179,4 +180,8 @@ class DecodeLoopGen:
         k = self._randn((sp.B, sp.L, sp.Hkv, sp.d)) + (a * (sp.k_focus * math.sqrt(sp.d))) * kd
         v = self._randn((sp.B, sp.L, sp.Hkv, sp.d))
         self.t += 1
+        if out is not None:
+            for dst, src in zip(out, (q, k, v)):
+                dst.copy_(src)
+            return out
         return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
