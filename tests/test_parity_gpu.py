@@ -292,3 +292,39 @@ def test_contiguous_pools():
     torch.cuda.synchronize()
     rep = compare_step(wl, np.arange(wl.B), st, out, res, wl.params["n_local"])
     _say(name, rep, res.counters)
+
+
+def test_token_budget_overflow():
+    """A batch larger than the scratch's token budget: the entries that fit (a prefix in
+    batch order) behave as the oracle's step on them alone; the rest are flagged
+    GP_REQ_OVERFLOW, report working sets of -1 and are left untouched."""
+    import dataclasses
+    from demand_paged_kv_amd import binding as Bd
+    from demand_paged_kv_amd.engine import BoundaryEngine
+    from synth import device as SD
+    name = "token_overflow"
+    wl = SW.direct_case(seed=zlib.crc32(name.encode()) % 10000, B=6, L=2, Hq=8, Hkv=2, d=64, P=16,
+                        ctx=(100, 400), grow_frac=0.2, spare_pages=30, name=name)
+    j = 3   # the fitting prefix holds a grow and two compactions
+    budget = sum(wl.n(b) for b in range(j))
+    sub = dataclasses.replace(wl, page_table=wl.page_table[:j], n_alloc=wl.n_alloc[:j], fill=wl.fill[:j],
+                              pos=wl.pos[:j], k_rows=wl.k_rows[:j], v_rows=wl.v_rows[:j],
+                              sum_s=wl.sum_s[:j], sum_l=wl.sum_l[:j])
+    res = O.boundary_step(sub, sub.sum_s, sub.sum_l, sub.params)
+    st = SD.upload(wl, "cuda")
+    eng = BoundaryEngine(st, wl.B, budget, Bd.params_from(wl.params))
+    out = eng.step(torch.arange(wl.B, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    rep = compare_step(sub, np.arange(j), st, out, res, wl.params["n_local"])
+    ws = out.ws.cpu().numpy()
+    status = out.status.cpu().numpy()
+    dec = out.decision.cpu().numpy()
+    table = st.page_table.cpu().numpy()
+    for b in range(j, wl.B):
+        assert status[b] == Bd.GP_REQ_OVERFLOW and dec[b] == Bd.GP_DECISION_COMPACT, (b, status[b], dec[b])
+        assert np.all(ws[b] == -1)
+        assert int(st.n_alloc[b]) == int(wl.n_alloc[b]) and int(st.fill[b]) == int(wl.fill[b])
+        assert np.array_equal(table[b], wl.page_table[b])
+        gk, gv = SD.read_rows(st, table[b], wl.n(b), wl.dtype)
+        assert np.array_equal(gk, wl.k_rows[b]) and np.array_equal(gv, wl.v_rows[b]), ("untouched", b)
+    _say(name, rep, res.counters, "status", status.tolist())
