@@ -23,9 +23,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kMfmaTok = 16;
 // Logits are staged in LDS and written out every kStageSteps steps: on this target loads
-// and stores share one completion counter, so a store in flight would turn every wait
-// for a key load into a wait for everything outstanding.  One more step of room holds
-// the range's partial last step.
+// and stores share one completion counter, so a store in flight turns the next wait for
+// a key load into a wait for everything outstanding (staging measured 1-5% faster than a
+// store per step).  One more step of room holds the range's partial last step.
 constexpr int kStageSteps = 16;
 constexpr int kStageBytes = (kStageSteps + 1) * kMfmaTok * kDists * 4;
 
@@ -95,7 +95,8 @@ struct MfmaSummaries {
 };
 
 // Steps [s0, s1) (16 tokens each) of a unit with n candidate slots: logits to lg_unit
-// ([logit_rows(n)][8], token-major; lanes 0..31 store), returns this lane's running max
+// ([logit_rows(n)][8], token-major; lanes 0..31 put each step's tile in `stage`, the
+// whole wave writes the stage out), returns this lane's running max
 // of its 4 rows (-inf if it saw no token).  Two key buffers alternate: the next step's
 // rows load while the current one is on the matrix cores, with no register copies
 // between them (a copy would wait for the loads in flight).  A step never crosses a
