@@ -44,6 +44,12 @@ MUTATIONS = {
     "shrink_releases_write_page": ("boundary_step", "old = int(table[b, a_old - 1])", "old = int(table[b, a_old])"),
     "shrink_on_one_page": ("boundary_step", "DECISION_SHRINK if A[b] >= 2 else DECISION_COMPACT",
                            "DECISION_SHRINK if A[b] >= 1 else DECISION_COMPACT"),
+    "cow_pages_descending": ("boundary_step", "        for j in need:\n", "        for j in need[::-1]:\n"),
+    "importance_of_logits": ("scan_request", "                        probs[l, g, 2 * j + sig] = a",
+                             "                        probs[l, g, 2 * j + sig] = lg"),
+    "write_page_not_candidate": ("boundary_step", "        n = int(wl.n_alloc[b]) * P + int(wl.fill[b])\n        e_req[b] = n",
+                                 "        n = int(wl.n_alloc[b]) * P\n        e_req[b] = n"),
+    "cow_checks_current_refcount": ("boundary_step", "if rc_snap[table[b, j]] > 1]", "if refcount[table[b, j]] > 1]"),
     "attention_scale_dropped": ("decode_attention", "softmax_stats(logits(qt[None, :], kf))",
                                 "softmax_stats(logits(qt[None, :], kf) * math.sqrt(d))"),
     "attention_query_not_rotated": ("decode_attention", "qt = rope_rotate(qf[l, h], cos_row, sin_row)",

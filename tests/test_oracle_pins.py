@@ -292,6 +292,28 @@ def test_importance_is_max_over_rows():
     assert np.array_equal(O.importance(a), [0.6, 0.7, 0.3])
 
 
+def test_importance_uses_probabilities_not_logits():
+    """R5: importance is the max over rows of softmax probabilities.  Row 0 peaks on slot 0
+    (logit 10/sqrt(8) against 0 elsewhere), row 2 is flat over slots 1..7 with larger raw
+    logits (20/sqrt(8)); the other rows are uniform.  In probability slot 0 matters most
+    (about 0.83 against 1/7), so keeping n - 1 slots evicts slot 1 (an exact tie among
+    slots 1..7 goes to the older slot); ranked by raw logits slot 0 would go."""
+    n, d = 8, 8
+    k = np.zeros((1, 1, n, d), np.float32)
+    k[0, 0, 0, 0] = 10.0
+    k[0, 0, 1:, 1] = 20.0
+    s = np.zeros((1, 4, d), np.float32)
+    l_ = np.zeros((1, 4, d), np.float32)
+    s[0, 0, 0] = 1.0      # head 0, short summary: row 0
+    s[0, 1, 1] = 1.0      # head 1, short summary: row 2
+    probs = O.scan_request(k, "f32", s, l_, None, None, 0.9, keep_logits=True)[5]
+    assert np.allclose(probs[0, 0].sum(axis=-1), 1.0)
+    imp = O.importance(probs[0, 0])
+    kept, ev, near = O.keep_set(imp, n - 1, 0)
+    assert ev.tolist() == [1]
+    assert imp[0] > 0.8 and abs(imp[1] - 1.0 / 7.0) < 1e-3
+
+
 def test_compaction_is_stable_gather():
     rows = np.arange(20 * 3).reshape(20, 3)
     kept = np.array([0, 2, 3, 7, 19])
