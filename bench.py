@@ -95,8 +95,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the boundary engine has no multi-GPU path "
-              "(each GPU would own its own pool; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the boundary engine has no multi-GPU path (each GPU "
+              "would own its pool and run the same calls on its own requests). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
