@@ -143,7 +143,8 @@ def softmax_stats(lg: np.ndarray):
 
 
 def working_set(a: np.ndarray, p: float, band: float = NEAR_TIE):
-    """Top-p attention working-set size [Summary: "Top-p attention working-set sizes"].
+    """Top-p attention working-set size [Summary: the boundary compares the two
+    summaries' Top-p working-set sizes].
 
     Reading R1: W = min{m >= 1 : sum of the m largest a_i >= p}, full sort, float64
     cumulative sum; p >= 1 gives n.  Also returns the sizes for p -/+ band, which
@@ -201,8 +202,9 @@ def policy_decision(delta: int, tau: int, policy: str = "growpage", u: float = 0
 
 
 def importance(a_group: np.ndarray) -> np.ndarray:
-    """Max-of-both importance per slot [Summary: "maximum of both temporal importance
-    scores"]; reading R5: max over the KV head's query heads and both summaries."""
+    """Max-of-both importance per slot [Summary: compaction ranks slots by the larger of
+    the two summaries' importance]; reading R5: max over the KV head's query heads and
+    both summaries."""
     return np.asarray(a_group, np.float64).max(axis=0)
 
 
