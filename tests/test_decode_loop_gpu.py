@@ -146,3 +146,71 @@ def test_decode_loop_full_shape_sampled():
              f"tracked {int(live.sum())}")
     assert boundaries == spec.steps // spec.P
     assert live.sum() >= 2
+
+
+def test_decode_loop_full_length_snapshots():
+    """The whole decode loop at its full size (128 requests x 36 layers x 4096 steps, 256
+    boundary batches).  The first, the last and every 32nd boundary batch is checked from
+    a snapshot: two requests drawn afresh for that batch are read back just before the
+    step and the oracle runs the step on them alone (summary update, append, boundary),
+    which works at any distance from the start because the summaries are bit-exact.  Pool
+    invariants are checked at every boundary.  A request whose decision the oracle finds
+    ambiguous (delta within rounding of tau) is checked for a delta inside the oracle's
+    range and left out of the element-wise comparison."""
+    from synth.decode_loop import DecodeLoopGen, DecodeSpec
+    spec = DecodeSpec(B=128, L=36, steps=4096, seed=4002)
+    gen = DecodeLoopGen(spec, "cuda")
+    st = gen.initial_state()
+    eng = _engine(spec, st)
+    req = torch.arange(spec.B, dtype=torch.int32, device="cuda")
+    fill = np.zeros(spec.B, np.int64)
+    n_local = spec.params["n_local"]
+    n_batches = spec.steps // spec.P
+    sampled = set(range(0, n_batches, 32)) | {n_batches - 1}
+    rng = np.random.default_rng(spec.seed)
+    boundaries = grows = checked = 0
+    _say(f"[decode-length] {spec.B} requests x {spec.L} layers x {spec.steps} steps; "
+         f"snapshots at batches {sorted(sampled)}")
+    for t in range(spec.steps):
+        q, k, v = gen.step()
+        at_boundary = fill[0] + 1 == spec.P
+        snap = at_boundary and boundaries in sampled
+        before = snapshot(st) if at_boundary else None
+        if snap:
+            track = np.sort(rng.choice(spec.B, 2, replace=False))
+            ost = DU.oracle_state(st, track)
+            ost.pos[:] = spec.prompt + t  # the step's position (the device's is set by the step)
+        bids, out = _gpu_step(eng, st, spec, t, q, k, v, fill, req)
+        if out is None:
+            assert not at_boundary
+            continue
+        assert bids.size == spec.B
+        dec = out.decision[: spec.B].cpu().numpy()
+        assert not out.status[: spec.B].cpu().numpy().any()
+        check_pool(st, before, dec, np.arange(spec.B))
+        grows += int(dec.sum())
+        if snap:
+            app, idx, sub, res = O.decode_step(ost, DU.bits(q[track]), "bf16", DU.bits(k[track]),
+                                               DU.bits(v[track]), spec.params)
+            assert app.all() and idx.size == track.size
+            s_gpu = st.sum_s[torch.as_tensor(track, device="cuda")].cpu().numpy()
+            assert np.array_equal(s_gpu.view(np.uint32), ost.sum_s.view(np.uint32)), t
+            keep = np.flatnonzero(~res.ambiguous)
+            delta = out.delta[: spec.B].cpu().numpy()
+            for i in np.flatnonzero(res.ambiguous):
+                assert res.delta_lo[i] <= delta[track[i]] <= res.delta_hi[i], (t, track[i])
+                _say(f"[decode-length] step {t}: request {track[i]} has an ambiguous decision")
+            if keep.size == track.size:
+                rep = compare_requests(sub, track, st, out, res, n_local)
+            elif keep.size:
+                sub_k = sub.subset(keep)
+                res_k = O.boundary_step(sub_k, sub_k.sum_s, sub_k.sum_l, spec.params)
+                rep = compare_requests(sub_k, track[keep], st, out, res_k, n_local)
+            checked += int(keep.size)
+            _say(f"[decode-length] step {t}: batch {boundaries} checked requests "
+                 f"{track[keep].tolist()} (keep-set near-ties {rep.ev_near if keep.size else 0}); "
+                 f"grows so far {grows}")
+        boundaries += 1
+    assert boundaries == n_batches
+    assert checked >= len(sampled)
+    assert 0 < grows < boundaries * spec.B
