@@ -11,7 +11,7 @@ import pytest
 from tests.oracle_mutations import MUTATIONS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-PINS = ["tests/test_oracle_pins.py", "tests/test_pool_replay.py"]
+PINS = ["tests/test_oracle_pins.py", "tests/test_pool_replay.py", "tests/test_oracle_properties.py"]
 
 
 def _run(name):
