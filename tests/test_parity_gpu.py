@@ -123,6 +123,8 @@ CASES = [
     ("p256_cow", dict(B=6, L=1, Hq=8, Hkv=2, d=64, P=256, grow_frac=0.2, prefix_groups=2, prefix_pages=2,
                       ctx=(300, 1500), spare_pages=12, params=dict(SW.PARAMS_PAPER))),
     ("p128_f32", dict(B=4, L=2, Hq=8, Hkv=2, d=128, P=128, dtype="f32", ctx=(100, 2000))),
+    # 128K-token units: a unit's logits (4 MB) far beyond the selection's LDS buffers
+    ("long_unit_128k", dict(B=2, L=1, Hq=32, Hkv=8, d=128, P=16, ctx=(131072, 131072), grow_frac=0.5)),
 ]
 
 
