@@ -256,7 +256,8 @@ gp_status gp_decode_attention(const gp_kv* kv, const gp_pages* pages, const void
   if (n_req == 0) return GP_OK;
   if (!q || !req_ids || !out) return GP_ERR_INVALID;
   if (q_dtype != GP_F32 && q_dtype != GP_BF16) return GP_ERR_INVALID;
-  if (rope_cos && (!rope_sin || !pos || rope_max_pos <= 0)) return GP_ERR_INVALID;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return GP_ERR_INVALID;
+  if (rope_cos && (!pos || rope_max_pos <= 0)) return GP_ERR_INVALID;
   const Geo g = make_geo(kv, pages, req_ids, n_req);
   return from_hip(launch_decode_attention(g, q, q_dtype, q_stride_req, q_stride_layer, q_stride_head,
                                           rope_cos, rope_sin, rope_max_pos, pos, out,

@@ -25,6 +25,11 @@
  *   - `req_ids[b]` (b < n_req) names the request slot of batch entry b; all
  *     per-request state (summaries, page-table rows, n_alloc, fill) is indexed by slot,
  *     all outputs by batch entry.  Slots in one call must be distinct.
+ *   - Device-resident state is trusted, not validated (checking it would need a copy to
+ *     the host): slots req_ids[b] in [0, max_req); 0 <= n_alloc[r] < max_pages;
+ *     0 <= fill[r] <= P; page ids in page_table[r][0 .. n_alloc[r]] in [0, num_pages);
+ *     refcounts and the free stack consistent with the page tables; pos[b] >= 0.
+ *     Values outside these ranges make the kernels read or write out of bounds.
  *
  * Paged KV model (the write-page model).  Request r owns n_alloc[r] = A allocation
  * pages page_table[r][0..A-1] plus one write page page_table[r][A] holding fill[r]
@@ -274,7 +279,8 @@ gp_status gp_append_kv(const gp_kv* kv, const gp_pages* pages, const void* k_new
  * req_ids[b]), layer l and query head h: out[b][l][h][:] = sum_i a_i v_i over the
  * request's n = n_alloc[r]*P + fill[r] slots, a = softmax(qr . k_i / sqrt(d)), where qr
  * is q[b][l][h] rotated to pos[r] (rotate-half pairs i, i + d/2, caller's table as in
- * gp_boundary_scan; rope_cos == NULL: identity).  q: element strides like
+ * gp_boundary_scan: both tables or neither, neither = identity; with tables, pos is
+ * required, else GP_ERR_INVALID).  q: element strides like
  * gp_update_summaries, bf16 or float32; out: [n_req][L][Hq][d] float32 (zeros for n ==
  * 0).  Reads the pool only. */
 gp_status gp_decode_attention(const gp_kv* kv, const gp_pages* pages, const void* q, int32_t q_dtype,

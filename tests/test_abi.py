@@ -96,6 +96,12 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert lib.gp_update_summaries(0x1000, 1, 4, 4, 6, 0x2000, 1, 2, 8, 64, 0x3000, 0x4000, P(prm), None) == B.GP_ERR_INVALID
     assert lib.gp_update_summaries(0x1000, 1, 4, 4, 4, 0x2000, 0, 2, 8, 64, 0x3000, 0x4000, P(prm), None) == B.GP_OK
     assert lib.gp_append_kv(P(kv), P(pg), None, 0x10, 0x9000, 1, None, None) == B.GP_ERR_INVALID
+    # decode attention: a rotation table needs both halves and the positions
+    att = lambda cos, sin, pos: lib.gp_decode_attention(P(kv), P(pg), 0x9000, B.GP_BF16, 4096, 512, 128,
+                                                        0xa000, 1, cos, sin, 100, pos, 0xb000, None)
+    assert att(None, 0xd000, 0xe000) == B.GP_ERR_INVALID
+    assert att(0xd000, None, 0xe000) == B.GP_ERR_INVALID
+    assert att(0xd000, 0xd800, None) == B.GP_ERR_INVALID
     # SHRINK: the flag is 0 or 1, and the keep-sets the scan sized must match the policy
     assert lib.gp_boundary_scan(*args(pr=B.params(shrink=2))) == B.GP_ERR_INVALID
     sh = B.params(shrink=1)
