@@ -70,6 +70,10 @@ def parse():
                          "physical pages behind ordinary allocations)")
     ap.add_argument("--schedules", default="serial,overlap",
                     help="overlap workload: schedules to run (serial, overlap)")
+    ap.add_argument("--placements", type=int, default=0,
+                    help="boundary sweep on this many fresh K/V pool placements (spacer allocations "
+                         "of 1-20 GiB between them): per-placement step and gather times on their "
+                         "own line, to show how the physical pages set the gather's speed")
     ap.add_argument("--paper", action="store_true",
                     help="boundary sweep at the pages' operating point (KV block 256, p 0.99, quota 64), "
                          "reported on its own line")
@@ -101,6 +105,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.placements > 0:
+        placements(args)
         return
     if args.workload == "decode_loop":
         decode_loop(args)
@@ -235,6 +242,65 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(gw, backup, args.cpu_budget)
     print(json.dumps(result), flush=True)
+
+
+def placements(args):
+    """The boundary sweep on several fresh physically contiguous pool placements in one
+    process: the same batch (state restored) timed per placement.  Between placements a
+    spacer allocation of a seeded random size moves where the next pools land."""
+    import numpy as np
+    import torch
+
+    from demand_paged_kv_amd import binding as Bd
+    from demand_paged_kv_amd import pool as PM
+    from demand_paged_kv_amd.engine import BoundaryEngine
+    from synth import gpu_workloads as GW
+
+    Bd.load()
+    gw = GW.boundary_sweep(seed=args.seed, contiguous=True)
+    st = gw.st
+    backup = GW.StateBackup(st)
+    shape = tuple(st.k_pool.shape)
+    st.k_pool = st.v_pool = None
+    torch.cuda.synchronize()
+    req = torch.arange(gw.B, dtype=torch.int32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    rng = np.random.default_rng(args.seed)
+    spacer = None
+    out = []
+    for i in range(args.placements):
+        k, kk = PM.empty(shape, torch.bfloat16, "cuda", True)
+        v, vk = PM.empty(shape, torch.bfloat16, "cuda", True)
+        st.k_pool, st.v_pool = k, v
+        eng = BoundaryEngine(st, gw.B, gw.total_tokens(), Bd.params_from(gw.params))
+        steps, moves = [], []
+        for _ in range(max(1, args.steps)):
+            backup.restore()
+            torch.cuda.synchronize()
+            ev[0].record()
+            eng.scan(req)
+            eng.decide(req)
+            eng.compact_prepare(req)
+            ev[1].record()
+            eng.compact_move(req)
+            ev[2].record()
+            torch.cuda.synchronize()
+            steps.append(ev[0].elapsed_time(ev[2]))
+            moves.append(ev[1].elapsed_time(ev[2]))
+        out.append({"placement": i, "pool_memory": "contiguous" if kk == vk == "contiguous" else "ordinary",
+                    "ms_per_step": round(float(np.mean(steps)), 4), "compact_move_ms": round(float(np.mean(moves)), 4)})
+        log(f"placement {i}: step {out[-1]['ms_per_step']:.3f} ms, gather {out[-1]['compact_move_ms']:.3f} ms")
+        del eng
+        st.k_pool = st.v_pool = None
+        del k, v
+        spacer = None
+        torch.cuda.synchronize()
+        spacer, _ = PM.empty((int(rng.integers(1, 21)) << 29,), torch.bfloat16, "cuda", True)
+    print(json.dumps({"metric": "boundary sweep step time per K/V pool placement (ms)", "higher_is_better": False,
+                      "config": {"workload": "boundary_sweep: 64 requests x 32 layers, 32q/8kv heads, d128, bf16 "
+                                             "K/V, page 16, fresh contiguous pools per placement",
+                                 "steps_per_placement": max(1, args.steps), "seed": args.seed},
+                      "placements": out}), flush=True)
 
 
 def decode_loop(args):
