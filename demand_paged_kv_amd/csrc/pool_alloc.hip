@@ -1,9 +1,9 @@
 // Physically contiguous device memory for the K/V pools (a deployment helper, not part of
 // the boundary path).  The boundary kernels address pool pages at random, and the row
 // moves of a compaction run at one of a few speeds set by the physical pages behind the
-// pools; on MI355X contiguous pools landed in the fast one somewhat more often than
-// ordinary allocations.  The two functions have the signatures of a PyTorch pluggable
-// allocator.
+// pools (on MI355X the slower placements wait longer for DRAM read credits); contiguity
+// did not reliably change which speed a placement gets.  The two functions have the
+// signatures of a PyTorch pluggable allocator.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

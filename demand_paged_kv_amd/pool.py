@@ -1,7 +1,7 @@
 """Physically contiguous device memory for K/V pools, from the library's
 gp_contiguous_malloc / gp_contiguous_free.  Allocation plumbing only: the compaction's
 row moves address pool pages at random, and their speed depends on the physical pages
-behind the pools (contiguous pools were fast somewhat more often); the kernels
+behind the pools, which contiguity did not reliably change in measurements; the kernels
 themselves work on any device memory.
 
 The memory is handed to torch through the CUDA array interface, so torch's own caching

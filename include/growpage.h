@@ -259,7 +259,7 @@ gp_status gp_compact_move(const gp_kv* kv, const gp_pages* pages, const int32_t*
  * for the K/V pools, with the signatures of a PyTorch pluggable allocator
  * (torch.cuda.memory.CUDAPluggableAllocator).  The compaction's row moves address pool
  * pages at random, and their speed depends on the physical pages behind the pools
- * (contiguous pools were fast somewhat more often than ordinary ones).  Returns
+ * (contiguity did not reliably change it in measurements).  Returns
  * NULL when the device cannot supply `size` contiguous bytes; the caller then allocates
  * ordinary memory.  The stream argument is unused. */
 void* gp_contiguous_malloc(int64_t size, int32_t device, void* stream);
