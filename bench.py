@@ -420,7 +420,7 @@ def decode_loop(args):
 def policies(args):
     """The decode loop (128 requests x 36 layers from 1024-token prompts, --decode-steps
     steps) under each decision policy: GrowPage's own rule, RANDOM at GrowPage's measured
-    grow ratio (frequency-matched), INVERSE, ALWAYS_COMPACT and SHRINK.  Reports grow (and
+    grow ratio (same grow frequency, random timing), INVERSE, ALWAYS_COMPACT and SHRINK.  Reports grow (and
     shrink) ratios and pages in use at the end.  For GrowPage's run it also reports how
     the boundary signal delta_t ranks against the change of the recent working set over
     the next h boundaries, sum W_S(t+h) - sum W_L(t) (Spearman rho and sign agreement) --

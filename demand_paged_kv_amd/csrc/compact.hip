@@ -1,7 +1,8 @@
-// Compaction within the current allocation (GrowPage review on evolve.pub, "Summary":
-// historical KV states are compacted inside the allocation using the maximum of both
-// temporal importance scores; FAQ "Is GrowPage's code available?": local retention
-// quota 64; abstract: page-level integration keeps prefix caching).
+// Compaction inside the pages a request already holds (GrowPage review on evolve.pub,
+// "Summary": a request that does not grow packs its older cache entries into its current
+// pages, slots ranked by the larger of the two summaries' importance; FAQ "Is GrowPage's
+// code available?": 64 recent tokens always kept; abstract: the method works on
+// PagedAttention's pages, so prefix sharing survives, here through copy-on-write).
 //
 // Launch sequence for one batch (all on the caller's stream, no host round trip):
 //   (the keep-sets -- the n-k least important candidate slots of each (entry, layer,

@@ -1,6 +1,6 @@
-// Boundary decision and grow (GrowPage review on evolve.pub, "Summary": a larger recent
-// working set triggers allocation of one extra physical page, otherwise compact; FAQ
-// "Is GrowPage's code available?": demand threshold tau 0).
+// Boundary decision and grow (GrowPage review on evolve.pub, "Summary": the request gets
+// one more physical page when the fast summary's working set is the larger one, and is
+// compacted otherwise; FAQ "Is GrowPage's code available?": threshold tau 0).
 //
 // delta_b = sum over layers and query heads of (W_short - W_long); grow iff delta > tau
 // (or, for the ablation policies the pages compare: iff -delta > tau, iff a uniform draw

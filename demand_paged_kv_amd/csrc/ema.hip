@@ -1,6 +1,6 @@
 // Summary update: S <- beta_s*S + (1-beta_s)*q and L <- beta_l*L + (1-beta_l)*q
-// (GrowPage review on evolve.pub, "Summary": two exponentially smoothed pre-RoPE query
-// summaries; FAQ "Is GrowPage's code available?": beta 0.9 / 0.999).
+// (GrowPage review on evolve.pub, "Summary": two moving averages of the queries, taken
+// before RoPE; FAQ "Is GrowPage's code available?": factors 0.9 and 0.999).
 //
 // Float32, each product and the sum rounded on their own (no contraction), so the
 // result is bit-identical to any IEEE implementation of the same expression.  Pure

@@ -1,6 +1,6 @@
 // Working sets and keep-sets of one boundary batch, from the logits the scan wrote.
-// (GrowPage review on evolve.pub, "Summary": Top-p attention working-set sizes of the
-// two summaries; compaction keeps the slots with the maximum of both importance scores;
+// (GrowPage review on evolve.pub, "Summary": a Top-p working-set size per summary; a
+// compaction keeps the slots ranked highest by the larger of the two importances;
 // FAQ "Is GrowPage's code available?": local retention quota.)
 //
 // One 256-thread block per (entry, layer, KV head) unit, two reads of the unit's logits

@@ -1,7 +1,7 @@
 // Boundary scan: logits of both summaries against every retained key, per-head softmax
 // statistics and the Top-p attention working-set size of each summary.
-// (GrowPage review on evolve.pub, "Summary": compare the Top-p attention working-set
-// sizes induced by the short- and long-timescale summaries, kept pre-RoPE.)
+// (GrowPage review on evolve.pub, "Summary": the decision weighs the Top-p working set
+// of the fast summary against that of the slow one, both summaries kept before RoPE.)
 //
 // plan_kernel    1 block: candidate slots n of every batch entry, scratch offsets and a
 //                longest-first order of the entries.

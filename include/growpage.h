@@ -3,8 +3,8 @@
  * AMD Instinct MI355X (CDNA4, gfx950).
  *
  * What the engine computes (GrowPage review on evolve.pub, section "Summary", and the
- * paper's abstract): every request keeps two exponentially smoothed pre-RoPE query
- * summaries per query head (short and long timescale).  When the request's last KV
+ * paper's abstract): every request keeps two moving averages of its queries per query
+ * head, one fast and one slow, taken before RoPE.  When the request's last KV
  * page fills (a capacity boundary), both summaries are scored against every retained
  * key, the Top-p attention working-set size of each summary's softmax is taken, and
  * the request either gets one more physical page (the recent working set is larger)
@@ -141,7 +141,7 @@ const char* gp_last_hip_error_string(void);
 /* Summary update, for every batch entry b, layer l, query head h and element i:
  *   S <- beta_s*S + (1-beta_s)*q,   L <- beta_l*L + (1-beta_l)*q
  * in float32 with each product and the sum rounded separately and (1-beta) formed in
- * float32 (GrowPage review, "Summary": exponentially smoothed pre-RoPE summaries).
+ * float32 (GrowPage review, "Summary": moving averages of the queries before RoPE).
  * q: [n_req] x [L] x [Hq] x [d] of q_dtype at element strides q_stride_req,
  *    q_stride_layer, q_stride_head (d contiguous, 8-byte aligned rows).
  * sum_s, sum_l: [max_req][L][Hq][d] float32, updated in place at row req_ids[b].
@@ -156,8 +156,7 @@ gp_status gp_update_summaries(const void* q, int32_t q_dtype, int64_t q_stride_r
  * requests whose candidate slots sum to at most max_total_tokens. */
 size_t gp_scratch_bytes(const gp_kv* kv, int32_t n_req, int64_t max_total_tokens);
 
-/* Boundary scan (GrowPage review, "Summary": Top-p working-set sizes induced by the two
- * summaries).  For each batch entry b (slot r = req_ids[b]), layer l and query head h,
+/* Boundary scan (GrowPage review, "Summary": one Top-p working-set size per summary).  For each batch entry b (slot r = req_ids[b]), layer l and query head h,
  * both summaries are rotated to position pos[r] (pos: [max_req] int32 by slot; positions
  * outside the table are clamped to it) with rotate-half pairs (i, i+d/2) and the caller's
  * table rope_cos/rope_sin [rope_max_pos][d/2] float32 (both NULL = no rotation), scored
@@ -178,8 +177,8 @@ gp_status gp_boundary_scan(const gp_kv* kv, const gp_pages* pages, const int32_t
                            float* stats_out, void* scratch, size_t scratch_bytes,
                            int64_t max_total_tokens, void* stream);
 
-/* Decision and grow (GrowPage review, "Summary": a larger recent working set triggers
- * one extra physical page; FAQ: tau).  delta_out[b] = sum over l, h of
+/* Decision and grow (GrowPage review, "Summary": one more page when the fast summary's
+ * working set is the larger; FAQ: tau).  delta_out[b] = sum over l, h of
  * (ws[b][l][h][0] - ws[b][l][h][1]); decision GROW iff delta > tau.  Grows pop the free
  * stack in batch order; with the stack empty (or page_table row full) the request is
  * compacted instead and flagged GP_REQ_GROW_DENIED.  Requests with fill != P are
@@ -198,7 +197,7 @@ gp_status gp_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_req, in
  * GrowPage differ from Zipage?" for the fixed budget). */
 typedef enum {
   GP_POLICY_GROWPAGE = 0,        /* grow iff delta > tau (gp_decide)                         */
-  GP_POLICY_RANDOM = 1,          /* grow iff rand_u[b] < grow_prob (frequency-matched random) */
+  GP_POLICY_RANDOM = 1,          /* grow iff rand_u[b] < grow_prob (random timing, matched frequency) */
   GP_POLICY_INVERSE = 2,         /* grow iff -delta > tau (signal direction reversed)        */
   GP_POLICY_ALWAYS_COMPACT = 3,  /* never grow (fixed per-request budget)                    */
   GP_POLICY_SHRINK = 4           /* grow iff delta > tau; otherwise (also after a denied grow)
@@ -221,8 +220,8 @@ gp_status gp_decide_policy(const int32_t* ws, const int32_t* req_ids, int32_t n_
                            uint8_t* decision_out, int32_t* delta_out, int32_t* status_out,
                            int32_t* counters_out, void* stream);
 
-/* Compaction (GrowPage review, "Summary": compact within the current allocation by the
- * maximum of both temporal importance scores; abstract: prefix caching preserved).
+/* Compaction (GrowPage review, "Summary": pack the kept slots into the request's current
+ * pages, ranked by the larger of the two importances; abstract: prefix sharing survives).
  * For every batch entry with decision COMPACT or SHRINK and fill == P: takes the n - k
  * evicted slots of each (layer, KV head) (k = A*P, or (A-1)*P for SHRINK, whose
  * allocation page A-1 then loses this reference and whose write page moves to

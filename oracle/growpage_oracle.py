@@ -7,12 +7,12 @@ numpy (matmul and sort are the only library primitives), in float64 except where
 reading fixes the precision.
 
 What the pages say (cited by page title and section; the pages carry no formulas):
-  [Summary]  GrowPage review on evolve.pub, section "Summary": at each PagedAttention
-             capacity boundary, compare the Top-p attention working-set sizes induced
-             by two exponentially smoothed query summaries (short and long timescale,
-             beta 0.9 / 0.999, kept pre-RoPE); a larger recent working set allocates
-             one extra physical page, otherwise history is compacted inside the
-             current allocation using the maximum of both temporal importance scores.
+  [Summary]  GrowPage review on evolve.pub, section "Summary": a request keeps two
+             moving averages of its queries (factors 0.9 and 0.999, before RoPE); at
+             each capacity boundary of its paged cache each average gets a Top-p
+             working-set size; if the fast one's is larger the request receives one
+             more physical page, otherwise its older entries are packed into the pages
+             it holds, slots ranked by the larger of the two averages' importance.
   [FAQ-impl] Same page, FAQ "Is GrowPage's code available?": beta_S 0.9, beta_L
              0.999, Top-p 0.99, demand threshold tau 0, local retention quota 64,
              KV block 256.
@@ -89,7 +89,7 @@ def query_f32(q: np.ndarray, dtype: str) -> np.ndarray:
 
 # ----------------------------------------------------------------------------- steps
 def ema_update(s: np.ndarray, q: np.ndarray, beta: float) -> np.ndarray:
-    """One summary update [Summary: exponentially smoothed query summaries; FAQ-impl: betas].
+    """One summary update [Summary: moving averages of the queries; FAQ-impl: factors].
 
     Reading R3: s <- beta*s + (1-beta)*q in float32, each product and the sum rounded
     on their own; (1-beta) is itself the float32 difference of 1 and float32(beta).
