@@ -245,8 +245,9 @@ def main():
 
 
 def placements(args):
-    """The boundary sweep on several fresh physically contiguous pool placements in one
-    process: the same batch (state restored) timed per placement.  Between placements a
+    """The boundary sweep on several fresh pool placements in one process (physically
+    contiguous pools unless --ordinary-pools): the same batch (state restored) timed per
+    placement.  Between placements a
     spacer allocation of a seeded random size moves where the next pools land."""
     import numpy as np
     import torch
@@ -257,7 +258,8 @@ def placements(args):
     from synth import gpu_workloads as GW
 
     Bd.load()
-    gw = GW.boundary_sweep(seed=args.seed, contiguous=True)
+    contiguous = not args.ordinary_pools
+    gw = GW.boundary_sweep(seed=args.seed, contiguous=contiguous)
     st = gw.st
     backup = GW.StateBackup(st)
     shape = tuple(st.k_pool.shape)
@@ -269,8 +271,8 @@ def placements(args):
     spacer = None
     out = []
     for i in range(args.placements):
-        k, kk = PM.empty(shape, torch.bfloat16, "cuda", True)
-        v, vk = PM.empty(shape, torch.bfloat16, "cuda", True)
+        k, kk = PM.empty(shape, torch.bfloat16, "cuda", contiguous)
+        v, vk = PM.empty(shape, torch.bfloat16, "cuda", contiguous)
         st.k_pool, st.v_pool = k, v
         eng = BoundaryEngine(st, gw.B, gw.total_tokens(), Bd.params_from(gw.params))
         steps, moves = [], []
@@ -295,10 +297,12 @@ def placements(args):
         del k, v
         spacer = None
         torch.cuda.synchronize()
-        spacer, _ = PM.empty((int(rng.integers(1, 21)) << 29,), torch.bfloat16, "cuda", True)
+        torch.cuda.empty_cache()  # ordinary pools: return the memory, so the next ones are fresh
+        spacer, _ = PM.empty((int(rng.integers(1, 21)) << 29,), torch.bfloat16, "cuda", contiguous)
     print(json.dumps({"metric": "boundary sweep step time per K/V pool placement (ms)", "higher_is_better": False,
                       "config": {"workload": "boundary_sweep: 64 requests x 32 layers, 32q/8kv heads, d128, bf16 "
-                                             "K/V, page 16, fresh contiguous pools per placement",
+                                             f"K/V, page 16, fresh {'contiguous' if contiguous else 'ordinary'} "
+                                             "pools per placement",
                                  "steps_per_placement": max(1, args.steps), "seed": args.seed},
                       "placements": out}), flush=True)
 
