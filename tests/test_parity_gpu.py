@@ -123,6 +123,10 @@ CASES = [
     ("p256_cow", dict(B=6, L=1, Hq=8, Hkv=2, d=64, P=256, grow_frac=0.2, prefix_groups=2, prefix_pages=2,
                       ctx=(300, 1500), spare_pages=12, params=dict(SW.PARAMS_PAPER))),
     ("p128_f32", dict(B=4, L=2, Hq=8, Hkv=2, d=128, P=128, dtype="f32", ctx=(100, 2000))),
+    # bf16 keys in pages that are not a multiple of 16 tokens: the vector-unit scan
+    ("bf16_d128_p24", dict(B=5, L=2, Hq=32, Hkv=8, d=128, P=24, ctx=(50, 1500))),
+    ("bf16_d64_p8_cow", dict(B=6, L=2, Hq=8, Hkv=2, d=64, P=8, ctx=(9, 700), grow_frac=0.3, prefix_groups=2,
+                             prefix_pages=2, spare_pages=24, params=dict(SW.PARAMS_DEFAULT, n_local=8))),
     # 128K-token units: a unit's logits (4 MB) far beyond the selection's LDS buffers
     ("long_unit_128k", dict(B=2, L=1, Hq=32, Hkv=8, d=128, P=16, ctx=(131072, 131072), grow_frac=0.5)),
 ]
