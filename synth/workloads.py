@@ -123,7 +123,7 @@ def _zipf_plant(rng, n, d, dirs_post, s_zipf, alpha=2.0, n_plant=None):
     k = rng.standard_normal((n, d))
     for u in dirs_post:
         rank = rng.permutation(n).astype(np.float64) + 1.0
-        mu = s_zipf * (math.log(n) - np.log(rank)) * math.sqrt(d) / alpha
+        mu = s_zipf * (math.log(max(n, 1)) - np.log(rank)) * math.sqrt(d) / alpha  # n = 0: no keys
         if n_plant is not None:
             mu = np.where(rank <= n_plant, mu, 0.0)
         k += mu[:, None] * u[None, :]
@@ -234,7 +234,7 @@ def direct_case(seed: int, B: int = 4, L: int = 2, Hq: int = 8, Hkv: int = 2, d:
                 spare_pages: int = 64, grow_frac: float = 0.3, rope: bool = True,
                 prefix_groups: int = 0, prefix_pages: int = 0, fill=None,
                 params: Optional[dict] = None, s_zipf=(0.8, 1.6), max_pages: Optional[int] = None,
-                name: str = "direct") -> Workload:
+                name: str = "direct", alloc=None) -> Workload:
     """Generic case with directly synthesised pre-RoPE summaries (the large-config recipe).
 
     Per (request, layer, query head) a unit direction u is drawn in the pre-RoPE frame;
@@ -242,12 +242,17 @@ def direct_case(seed: int, B: int = 4, L: int = 2, Hq: int = 8, Hkv: int = 2, d:
     requests draw b_S in [0.2, 0.8] and b_L in [1.5, 3]; concentrating ones b_S in
     [2, 5] and b_L in [0.5, 1.5].  Keys carry a Zipf(s) profile along each head's
     direction rotated to the request's position.  Optional prefix sharing: groups of
-    requests share their first ``prefix_pages`` pages (refcounted).
+    requests share their first ``prefix_pages`` pages (refcounted).  ``alloc`` sets each
+    request's allocation pages directly (0 allowed: a request holding only its write
+    page) instead of drawing them from ``ctx``.
     """
     rng = np.random.default_rng(seed)
     G = Hq // Hkv
     ctx_tok = np.exp(rng.uniform(math.log(ctx[0]), math.log(ctx[1]), size=B))
     A = np.maximum(np.ceil(ctx_tok / P).astype(np.int32), max(1, prefix_pages))
+    if alloc is not None:
+        A = np.asarray(alloc, np.int32)
+        assert A.shape == (B,) and A.min() >= (prefix_pages if prefix_groups else 0)
     fill = np.full(B, P, np.int32) if fill is None else np.asarray(fill, np.int32)
     n = A * P + fill
     pos = (n + rng.integers(0, 64, size=B)).astype(np.int32)

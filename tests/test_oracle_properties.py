@@ -99,6 +99,8 @@ def _references(table, n_alloc, num_pages):
 def test_boundary_step_keeps_the_pool_consistent(seed, B, P, spare, grow_frac, share, n_local, policy, data):
     fill = [data.draw(st.sampled_from([P, P, data.draw(st.integers(0, P - 1))])) for _ in range(B)]
     prefix = dict(prefix_groups=max(1, B // 3), prefix_pages=2) if share else {}
+    if not share and data.draw(st.booleans()):  # allocations drawn directly, zero pages included
+        prefix = dict(alloc=[data.draw(st.integers(0, 3)) for _ in range(B)])
     params = dict(SW.PARAMS_DEFAULT, n_local=n_local, policy=policy)
     wl = SW.direct_case(seed=seed, B=B, L=1, Hq=8, Hkv=2, d=64, P=P, ctx=(1, 120), spare_pages=spare,
                         grow_frac=grow_frac, fill=fill, params=params, **prefix)

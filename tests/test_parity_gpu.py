@@ -127,6 +127,9 @@ CASES = [
     ("bf16_d128_p24", dict(B=5, L=2, Hq=32, Hkv=8, d=128, P=24, ctx=(50, 1500))),
     ("bf16_d64_p8_cow", dict(B=6, L=2, Hq=8, Hkv=2, d=64, P=8, ctx=(9, 700), grow_frac=0.3, prefix_groups=2,
                              prefix_pages=2, spare_pages=24, params=dict(SW.PARAMS_DEFAULT, n_local=8))),
+    # requests holding only their write page (no allocation pages): they grow or keep nothing
+    ("zero_alloc", dict(B=6, L=2, Hq=8, Hkv=2, d=64, P=16, alloc=[0, 0, 0, 1, 3, 0], fill=[16, 16, 16, 16, 16, 5],
+                        grow_frac=0.6, params=dict(SW.PARAMS_DEFAULT, n_local=8))),
     # 128K-token units: a unit's logits (4 MB) far beyond the selection's LDS buffers
     ("long_unit_128k", dict(B=2, L=1, Hq=32, Hkv=8, d=128, P=16, ctx=(131072, 131072), grow_frac=0.5)),
 ]
@@ -264,6 +267,9 @@ SHRINK_CASES = [
     # 2P = 512 evicted slots per unit, the pages' operating point
     ("shrink_p256", dict(B=4, L=1, Hq=32, Hkv=8, d=128, P=256, ctx=(300, 2500), grow_frac=0.3,
                          params=dict(SW.PARAMS_DEFAULT, top_p=0.99, n_local=64))),
+    # no allocation pages and one page: both compact in place; two pages shrink
+    ("shrink_write_page_only", dict(B=6, L=2, Hq=8, Hkv=2, d=64, P=16, alloc=[0, 0, 1, 2, 3, 1], grow_frac=0.4,
+                                    params=dict(SW.PARAMS_DEFAULT, n_local=8))),
     # float32 keys, page 8 (the vector-unit scan), one-page allocations that compact in place
     ("shrink_f32_p8", dict(B=8, L=2, Hq=8, Hkv=2, d=64, P=8, dtype="f32", ctx=(4, 200), grow_frac=0.3,
                            params=dict(SW.PARAMS_DEFAULT, n_local=4))),
