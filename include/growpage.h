@@ -165,7 +165,8 @@ size_t gp_scratch_bytes(const gp_kv* kv, int32_t n_req, int64_t max_total_tokens
  * (s = 0 short, 1 long; top_p >= 1 gives n).  It also selects each (layer, KV head)'s
  * evicted slots for a compaction into k = A*P slots (A = n_alloc; k = (A-1)*P when
  * params->shrink and A >= 2).  stats_out (optional, may be NULL):
- * [n_req][L][Hq][2][2] float32 = (max logit, sum exp(logit - max)).  The logits and
+ * [n_req][L][Hq][2][2] float32 = (max logit, sum exp(logit - max)); an entry with no
+ * candidate slots (n = 0) gets working sets 0, max -INFINITY and sum 0.  The logits and
  * statistics are also kept in `scratch` for gp_compact, so the same scratch must be
  * passed to gp_compact unchanged.  The page state is only read.
  * Errors: GP_ERR_INVALID (NULL/shape), GP_ERR_SCRATCH (scratch too small),

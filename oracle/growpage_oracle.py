@@ -49,11 +49,14 @@ Readings taken where the pages are silent (each repeated where it is used):
       GROW_DENIED); a request whose copy-on-write demand exceeds the stack is left
       untouched (status DEFERRED).
   R16 SHRINK ablation [same page, "Strengths", item "Frequency-matched causal
-      ablations": SHRINK isolates the cost of irreversible shrinking]: grow iff
+      ablations": a policy whose budget can only go down]: grow iff
       delta > tau as GrowPage; every other request at its boundary with A >= 2
       keeps k = (A-1)*P slots by R6's rule in pages 0..A-2, drops its reference to
       allocation page A-1 and moves its write page into that page-table slot; with
       A < 2 it compacts in place.
+  R17 Empty request (no allocation pages, empty write page; the pages never meet
+      it): its working sets are 0 and each softmax row has max -inf (the max over
+      no logits) and sum 0 (the empty sum).
 """
 from __future__ import annotations
 
@@ -282,7 +285,8 @@ def scan_request(k_rows: np.ndarray, dtype: str, sum_s: np.ndarray, sum_l: np.nd
                 h = g * G + j
                 for sig, summ in enumerate((sum_s, sum_l)):
                     qt = rope_rotate(summ[l, h], cos_row, sin_row)
-                    if n == 0:
+                    if n == 0:  # reading R17: empty row, max -inf, sum 0, W 0
+                        M[l, h, sig] = -np.inf
                         continue
                     lg = logits(qt[None, :], kf)[0]
                     m_, z_, a = softmax_stats(lg)

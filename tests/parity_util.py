@@ -33,6 +33,18 @@ class Report:
     diverged: list = dataclasses.field(default_factory=list)   # requests whose keep-set took the other side of a near-tie
 
 
+
+def stat_errors(M_gpu, Z_gpu, M_ref, Z_ref):
+    """Relative errors of (max logit, sum exp); an empty row (reading R17: max -inf, sum 0)
+    must match exactly and counts as error 0."""
+    empty = np.isneginf(M_ref)
+    assert np.array_equal(np.isneginf(M_gpu), empty) and np.all(Z_gpu[empty] == 0), "empty-row statistics"
+    M_gpu, M_ref = np.where(empty, 0.0, M_gpu), np.where(empty, 0.0, M_ref)
+    Z_ref1 = np.where(empty, 1.0, Z_ref)
+    errM = np.abs(M_gpu - M_ref) / np.maximum(1.0, np.abs(M_ref))
+    errZ = np.abs(np.where(empty, 1.0, Z_gpu) - Z_ref1) / Z_ref1
+    return errM, errZ
+
 def snapshot(st):
     """Host copies of the page state (before a step)."""
     return dict(page_table=st.page_table.cpu().numpy().copy(), n_alloc=st.n_alloc.cpu().numpy().copy(),
@@ -62,9 +74,8 @@ def compare_step(wl, slots, st, out, res: O.StepResult, n_local: int, check_page
 
     # ---- softmax statistics
     M, Z = stats[..., 0], stats[..., 1]
-    errM = np.abs(M - res.M) / np.maximum(1.0, np.abs(res.M))
+    errM, errZ = stat_errors(M, Z, res.M, res.Z)
     assert errM.max() <= LOGIT_TOL, f"max logit error {errM.max()}"
-    errZ = np.abs(Z - res.Z) / res.Z
     assert errZ.max() <= Z_RTOL, f"sum-exp error {errZ.max()}"
 
     # ---- decisions
@@ -165,8 +176,7 @@ def compare_requests(wl, batch_idx, st, out, res: O.StepResult, n_local: int) ->
     rep.ws_total, rep.ws_near = int(res.W.size), int(near.sum())
     assert not (~near & (ws != res.W)).any(), "W mismatch"
     assert not (near & ((ws < res.W_lo) | (ws > res.W_hi))).any(), "W outside near-tie range"
-    errM = np.abs(stats[..., 0] - res.M) / np.maximum(1.0, np.abs(res.M))
-    errZ = np.abs(stats[..., 1] - res.Z) / res.Z
+    errM, errZ = stat_errors(stats[..., 0], stats[..., 1], res.M, res.Z)
     assert errM.max() <= LOGIT_TOL and errZ.max() <= Z_RTOL, (errM.max(), errZ.max())
     for i in range(len(idx)):
         assert not res.ambiguous[i], "ambiguous decision in the sample"
@@ -270,8 +280,7 @@ def compare_sampled(wl, batch_idx, st, out, params: dict) -> Report:
         rep.ws_near += int(near.sum())
         assert not (~near & (ws[b] != W)).any(), ("W mismatch", b)
         assert not (near & ((ws[b] < Wlo) | (ws[b] > Whi))).any(), ("W outside near-tie range", b)
-        errM = np.abs(stats[b][..., 0] - M) / np.maximum(1.0, np.abs(M))
-        errZ = np.abs(stats[b][..., 1] - Z) / Z
+        errM, errZ = stat_errors(stats[b][..., 0], stats[b][..., 1], M, Z)
         assert errM.max() <= LOGIT_TOL and errZ.max() <= Z_RTOL, (b, errM.max(), errZ.max())
         d0, dlo, dhi = O.delta_range(W, Wlo, Whi)
         assert dlo <= delta[b] <= dhi, (b, delta[b], dlo, dhi)

@@ -706,3 +706,12 @@ def test_decode_attention_rotates_the_query_like_the_keys():
     v32 = v.astype(np.float32).astype(np.float64)
     want = (math.exp(x) * v32[0, 0, 0] + v32[0, 0, 1]) / (math.exp(x) + 1.0)
     assert np.allclose(out[0, 0], want, atol=1e-5)
+
+
+def test_empty_request_statistics():
+    """Reading R17: a request with no candidate slots has working sets 0, max -inf and
+    sum 0 for every row (the identities of max and sum), and is never at a boundary."""
+    wl = SW.direct_case(seed=5, B=2, L=1, Hq=8, Hkv=2, d=64, P=16, alloc=[0, 1], fill=[0, 16])
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, wl.params)
+    assert np.all(res.W[0] == 0) and np.all(np.isneginf(res.M[0])) and np.all(res.Z[0] == 0)
+    assert res.status[0] & O.REQ_NOT_AT_BOUNDARY and np.all(np.isfinite(res.M[1]))

@@ -127,8 +127,9 @@ CASES = [
     ("bf16_d128_p24", dict(B=5, L=2, Hq=32, Hkv=8, d=128, P=24, ctx=(50, 1500))),
     ("bf16_d64_p8_cow", dict(B=6, L=2, Hq=8, Hkv=2, d=64, P=8, ctx=(9, 700), grow_frac=0.3, prefix_groups=2,
                              prefix_pages=2, spare_pages=24, params=dict(SW.PARAMS_DEFAULT, n_local=8))),
-    # requests holding only their write page (no allocation pages): they grow or keep nothing
-    ("zero_alloc", dict(B=6, L=2, Hq=8, Hkv=2, d=64, P=16, alloc=[0, 0, 0, 1, 3, 0], fill=[16, 16, 16, 16, 16, 5],
+    # requests holding only their write page (no allocation pages): they grow or keep nothing;
+    # the last one is empty (n = 0)
+    ("zero_alloc", dict(B=6, L=2, Hq=8, Hkv=2, d=64, P=16, alloc=[0, 0, 0, 1, 3, 0], fill=[16, 16, 16, 16, 16, 0],
                         grow_frac=0.6, params=dict(SW.PARAMS_DEFAULT, n_local=8))),
     # 128K-token units: a unit's logits (4 MB) far beyond the selection's LDS buffers
     ("long_unit_128k", dict(B=2, L=1, Hq=32, Hkv=8, d=128, P=16, ctx=(131072, 131072), grow_frac=0.5)),
