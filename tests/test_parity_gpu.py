@@ -127,6 +127,11 @@ CASES = [
     ("bf16_d128_p24", dict(B=5, L=2, Hq=32, Hkv=8, d=128, P=24, ctx=(50, 1500))),
     ("bf16_d64_p8_cow", dict(B=6, L=2, Hq=8, Hkv=2, d=64, P=8, ctx=(9, 700), grow_frac=0.3, prefix_groups=2,
                              prefix_pages=2, spare_pages=24, params=dict(SW.PARAMS_DEFAULT, n_local=8))),
+    # demand thresholds away from 0: positive deltas below tau compact, negative ones above it grow
+    ("tau_positive", dict(B=8, L=2, Hq=32, Hkv=8, d=128, P=16, ctx=(100, 1500), grow_frac=0.5,
+                          params=dict(SW.PARAMS_DEFAULT, tau=10000))),
+    ("tau_negative", dict(B=8, L=2, Hq=32, Hkv=8, d=128, P=16, ctx=(100, 1500), grow_frac=0.5,
+                          params=dict(SW.PARAMS_DEFAULT, tau=-16000))),
     # requests holding only their write page (no allocation pages): they grow or keep nothing;
     # the last one is empty (n = 0)
     ("zero_alloc", dict(B=6, L=2, Hq=8, Hkv=2, d=64, P=16, alloc=[0, 0, 0, 1, 3, 0], fill=[16, 16, 16, 16, 16, 0],
