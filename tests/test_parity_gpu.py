@@ -50,6 +50,41 @@ def test_ema_bit_exact(cfg):
     assert np.array_equal(l_gpu.view(np.uint32), l_ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("beta_s,beta_l", [(0.5, 1.0), (1.0, 0.1), (0.25, 0.99999994)])
+@pytest.mark.parametrize("q_dtype", ["f32", "bf16"])
+def test_ema_other_betas(beta_s, beta_l, q_dtype):
+    """Summary updates at other smoothing factors, from non-zero summaries: beta 1 keeps
+    a summary as it was, a factor one float32 ulp below 1 moves it by a rounded 1-beta;
+    bit-exact against the oracle's update."""
+    from demand_paged_kv_amd import binding as Bd
+    rng = np.random.default_rng(11)
+    n, L, Hq, d = 3, 2, 8, 128
+    qf = rng.standard_normal((n, L, Hq, d)).astype(np.float32)
+    if q_dtype == "bf16":
+        q = torch.from_numpy(qf).to(torch.bfloat16).cuda()
+        qh = q.float().cpu().numpy()
+    else:
+        q = torch.from_numpy(qf).cuda()
+        qh = qf
+    s0 = rng.standard_normal((n, L, Hq, d)).astype(np.float32)
+    l0 = rng.standard_normal((n, L, Hq, d)).astype(np.float32)
+    S, Lg = torch.from_numpy(s0.copy()).cuda(), torch.from_numpy(l0.copy()).cuda()
+    prm = Bd.params(beta_s, beta_l)
+    qd = Bd.GP_BF16 if q_dtype == "bf16" else Bd.GP_F32
+    req = torch.arange(n, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        Bd.update_summaries(q, qd, (q.stride(0), q.stride(1), q.stride(2)), req, n, L, Hq, d, S, Lg, prm)
+    torch.cuda.synchronize()
+    want_s, want_l = s0.copy(), l0.copy()
+    for _ in range(3):
+        want_s = O.ema_update(want_s, qh, beta_s)
+        want_l = O.ema_update(want_l, qh, beta_l)
+    assert np.array_equal(S.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    assert np.array_equal(Lg.cpu().numpy().view(np.uint32), want_l.view(np.uint32))
+    if beta_l == 1.0:
+        assert np.array_equal(Lg.cpu().numpy(), l0)
+
+
 def test_ema_strided_slots():
     """Strided q and scattered request slots update exactly the named rows."""
     from demand_paged_kv_amd import binding as Bd
