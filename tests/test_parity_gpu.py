@@ -188,6 +188,22 @@ def test_direct_cases(name, kw):
     _say(name, rep, res.counters)
 
 
+def test_rope_positions_clamped_to_the_table():
+    """Positions beyond the caller's rotation table use its last row: the scan on a table
+    cut short matches the oracle at the clamped positions (full table, same rows)."""
+    import dataclasses
+    wl = SW.direct_case(seed=321, B=6, L=2, Hq=32, Hkv=8, d=128, P=16, ctx=(100, 1200), grow_frac=0.5,
+                        params=dict(SW.PARAMS_DEFAULT, n_local=16))
+    T = int(np.median(wl.pos))
+    assert (wl.pos >= T).any() and (wl.pos < T - 1).any()
+    wl_gpu = dataclasses.replace(wl, rope_cos=wl.rope_cos[:T].copy(), rope_sin=wl.rope_sin[:T].copy())
+    wl_ref = dataclasses.replace(wl, pos=np.minimum(wl.pos, T - 1).astype(np.int32))
+    res = O.boundary_step(wl_ref, wl.sum_s, wl.sum_l, wl.params)
+    st, out, _ = run_step_gpu(wl_gpu)
+    rep = compare_step(wl_ref, np.arange(wl.B), st, out, res, wl.params["n_local"])
+    _say("rope clamp", rep, res.counters)
+
+
 def test_counters_config2():
     wl = SW.config2(seed=2001)
     s, l_ = O.ema_run(wl.queries, wl.q_dtype, wl.params["beta_s"], wl.params["beta_l"])
