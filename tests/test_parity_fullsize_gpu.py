@@ -12,12 +12,23 @@ from tests.parity_util import check_pool, compare_requests, snapshot
 pytestmark = pytest.mark.gpu
 
 
+def _bench_step(eng, req):
+    """One boundary batch with the calls bench.py times: scan, decide, compact_prepare,
+    compact_move (the split form of gp_compact)."""
+    eng.scan(req)
+    eng.decide(req)
+    eng.compact_prepare(req)
+    eng.compact_move(req)
+    torch.cuda.synchronize()
+    return eng.out
+
+
 def test_boundary_sweep_full_size_sampled():
     from demand_paged_kv_amd import binding as Bd
     from demand_paged_kv_amd.engine import BoundaryEngine
     from synth import gpu_workloads as GW
 
-    gw = GW.boundary_sweep(seed=3000)
+    gw = GW.boundary_sweep(seed=3000, contiguous=True)  # the bench's pools
     st = gw.st
     print(f"[fullsize] generated {gw.B} requests, {gw.total_tokens()} tokens", flush=True)
     order = np.argsort(-gw.n)
@@ -28,9 +39,8 @@ def test_boundary_sweep_full_size_sampled():
     before = snapshot(st)
     eng = BoundaryEngine(st, gw.B, gw.total_tokens(), Bd.params_from(gw.params))
     req = torch.arange(gw.B, dtype=torch.int32, device="cuda")
-    out = eng.step(req)
-    torch.cuda.synchronize()
-    print("[fullsize] step done; oracle on sample", sample, flush=True)
+    out = _bench_step(eng, req)
+    print(f"[fullsize] step done ({gw.pool_memory} pools); oracle on sample", sample, flush=True)
     res = O.boundary_step(wl, wl.sum_s, wl.sum_l, gw.params)
     rep = compare_requests(wl, sample, st, out, res, gw.params["n_local"])
     dec = out.decision.cpu().numpy()
@@ -41,13 +51,15 @@ def test_boundary_sweep_full_size_sampled():
 
 
 def test_paper_operating_point_full_size_sampled():
-    """The sweep's shape at the pages' operating point: KV block 256, p 0.99, quota 64."""
+    """The sweep's shape at the pages' operating point: KV block 256, p 0.99, quota 64
+    (bench.py --paper's batch, pools and calls)."""
     from demand_paged_kv_amd import binding as Bd
     from demand_paged_kv_amd.engine import BoundaryEngine
     from synth import gpu_workloads as GW
     from synth import workloads as SW
 
-    gw = GW.boundary_sweep(seed=3100, P=256, num_pages=1536, params=dict(SW.PARAMS_PAPER), name="paper_sweep")
+    gw = GW.boundary_sweep(seed=3100, P=256, num_pages=1536, params=dict(SW.PARAMS_PAPER), name="paper_sweep",
+                           contiguous=True)
     st = gw.st
     print(f"[paper] generated {gw.B} requests, {gw.total_tokens()} tokens", flush=True)
     order = np.argsort(-gw.n)
@@ -56,8 +68,7 @@ def test_paper_operating_point_full_size_sampled():
     wl = GW.to_host_workload(gw, sample)
     before = snapshot(st)
     eng = BoundaryEngine(st, gw.B, gw.total_tokens(), Bd.params_from(gw.params))
-    out = eng.step(torch.arange(gw.B, dtype=torch.int32, device="cuda"))
-    torch.cuda.synchronize()
+    out = _bench_step(eng, torch.arange(gw.B, dtype=torch.int32, device="cuda"))
     res = O.boundary_step(wl, wl.sum_s, wl.sum_l, gw.params)
     rep = compare_requests(wl, sample, st, out, res, gw.params["n_local"])
     dec = out.decision.cpu().numpy()
