@@ -68,7 +68,7 @@ def test_prefix_share_full_size_sampled():
 
     free, total = torch.cuda.mem_get_info()
     _say(f"[prefix-full] device memory free {free / 2**30:.1f} GiB of {total / 2**30:.1f} GiB")
-    gw = GW.prefix_share(seed=5000)
+    gw = GW.prefix_share(seed=5000, contiguous=True)  # the bench's pools
     st = gw.st
     torch.cuda.synchronize()
     _say(f"[prefix-full] generated {gw.B} requests, {gw.total_tokens()} tokens, pool {st.num_pages} pages, "
@@ -81,10 +81,15 @@ def test_prefix_share_full_size_sampled():
     shared = torch.as_tensor(np.flatnonzero(before["refcount"] > 1), device="cuda")
     k_shared, v_shared = st.k_pool[:, shared].clone(), st.v_pool[:, shared].clone()
     eng = BoundaryEngine(st, gw.B, gw.total_tokens(), Bd.params_from(gw.params))
-    out = eng.step(torch.arange(gw.B, dtype=torch.int32, device="cuda"))
+    req = torch.arange(gw.B, dtype=torch.int32, device="cuda")
+    eng.scan(req)  # the calls bench.py times (split compaction)
+    eng.decide(req)
+    eng.compact_prepare(req)
+    eng.compact_move(req)
     torch.cuda.synchronize()
+    out = eng.out
     c = dict(zip(Bd.COUNTER_NAMES, out.counters.cpu().numpy().tolist()))
-    _say(f"[prefix-full] step done: {c}; oracle on sample {sample}")
+    _say(f"[prefix-full] step done ({gw.pool_memory} pools): {c}; oracle on sample {sample}")
     assert torch.equal(st.k_pool[:, shared], k_shared) and torch.equal(st.v_pool[:, shared], v_shared), \
         "a shared page changed"
     del k_shared, v_shared
