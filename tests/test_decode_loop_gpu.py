@@ -158,8 +158,8 @@ def test_decode_loop_full_length_snapshots():
     ambiguous (delta within rounding of tau) is checked for a delta inside the oracle's
     range and left out of the element-wise comparison."""
     from synth.decode_loop import DecodeLoopGen, DecodeSpec
-    spec = DecodeSpec(B=128, L=36, steps=4096, seed=4002)
-    gen = DecodeLoopGen(spec, "cuda")
+    spec = DecodeSpec(B=128, L=36, steps=4096, seed=4000)  # bench.py --workload decode_loop's loop
+    gen = DecodeLoopGen(spec, "cuda", contiguous=True)
     st = gen.initial_state()
     eng = _engine(spec, st)
     req = torch.arange(spec.B, dtype=torch.int32, device="cuda")
