@@ -28,6 +28,8 @@ CASES = [
     ("f32_d64_norope", dict(B=3, L=2, Hq=8, Hkv=2, d=64, P=16, dtype="f32", rope=False)),
     ("tiny_partial_pages", dict(B=6, L=1, Hq=8, Hkv=2, d=64, P=16, ctx=(1, 20), fill=[0, 3, 16, 1, 7, 15])),
     ("p256", dict(B=3, L=1, Hq=32, Hkv=8, d=128, P=256, ctx=(300, 2000))),
+    # no allocation pages: an empty request (zeros), a partial and a full write page
+    ("write_page_only", dict(B=4, L=2, Hq=8, Hkv=2, d=64, P=16, alloc=[0, 0, 0, 2], fill=[0, 5, 16, 7])),
 ]
 
 
