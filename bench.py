@@ -304,6 +304,9 @@ def placements(args):
                                              f"K/V, page 16, fresh {'contiguous' if contiguous else 'ordinary'} "
                                              "pools per placement",
                                  "steps_per_placement": max(1, args.steps), "seed": args.seed},
+                      "median_ms_per_step": round(float(np.median([p["ms_per_step"] for p in out])), 4),
+                      "min_ms_per_step": min(p["ms_per_step"] for p in out),
+                      "max_ms_per_step": max(p["ms_per_step"] for p in out),
                       "placements": out}), flush=True)
 
 
