@@ -52,14 +52,17 @@ def parse():
                     help="layer-tokens of oracle work in the CPU baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 4 GiB device copy (HBM counter calibration)")
-    ap.add_argument("--workload", choices=("boundary_sweep", "decode_loop", "prefix_share", "policies", "overlap"),
+    ap.add_argument("--workload", choices=("boundary_sweep", "decode_loop", "prefix_share", "policies", "overlap",
+                                           "one_layer"),
                     default="boundary_sweep",
                     help="boundary_sweep (default, the headline line); decode_loop (the 36-layer decode "
                          "loop: 128 requests x 4096 steps) or prefix_share (256 requests x 36 layers, page "
                          "32, shared 2048-token prefixes, pool at 80%% of demand; one shot) or policies (the "
                          "decode loop under each decision policy: grow ratios, and the signal's rank "
                          "correlation with the later working set) or overlap (decode attention with the "
-                         "boundary engine serial vs on a second stream), each reported on its own line")
+                         "boundary engine serial vs on a second stream) or one_layer (16 requests, one layer, "
+                         "summaries from 256 decode queries: a batch small enough to be bound by launch "
+                         "latency), each reported on its own line")
     ap.add_argument("--decode-steps", type=int, default=4096)
     ap.add_argument("--graphs", action="store_true",
                     help="decode_loop: replay each step from HIP graphs (one launch per step) "
@@ -120,6 +123,9 @@ def main():
         return
     if args.workload == "overlap":
         overlap(args)
+        return
+    if args.workload == "one_layer":
+        one_layer(args)
         return
     import numpy as np
     import torch
@@ -242,6 +248,64 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(gw, backup, args.cpu_budget)
     print(json.dumps(result), flush=True)
+
+
+def one_layer(args):
+    """One layer, 16 requests (32/8 heads, d 128, bf16, page 16, contexts log-uniform in
+    512-8192 tokens, page ids from a shuffled 65,536-page pool): the summaries are built
+    on the GPU by gp_update_summaries from 256 bf16 decode queries, then the boundary
+    batch is timed like the sweep's (state restored between steps).  About 45K tokens, so
+    the step is bound by launch latency rather than HBM; reported, not a target."""
+    import numpy as np
+    import torch
+
+    from demand_paged_kv_amd import binding as Bd
+    from demand_paged_kv_amd.engine import BoundaryEngine
+    from synth import device as SD
+    from synth import gpu_workloads as GW
+    from synth import workloads as SW
+
+    Bd.load()
+    wl = SW.config2(seed=2001)
+    st = SD.upload(wl, "cuda")
+    eng = BoundaryEngine(st, wl.B, wl.total_tokens(), Bd.params_from(wl.params))
+    req = torch.arange(wl.B, dtype=torch.int32, device="cuda")
+    q = torch.from_numpy(np.ascontiguousarray(wl.queries).view(np.int16)).view(torch.bfloat16).to("cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for t in range(q.shape[0]):
+        eng.update_summaries(q[t], req)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ema_ms = ev[0].elapsed_time(ev[1]) / q.shape[0]
+    backup = GW.StateBackup(st)
+    steps = max(1, args.steps) * 10
+    times = []
+    for i in range(args.warmup + steps):
+        backup.restore()
+        torch.cuda.synchronize()
+        ev[0].record()
+        eng.scan(req)
+        eng.decide(req)
+        eng.compact_prepare(req)
+        eng.compact_move(req)
+        ev[1].record()
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            times.append(ev[0].elapsed_time(ev[1]))
+    ms = float(np.mean(times))
+    c = dict(zip(Bd.COUNTER_NAMES, [int(x) for x in eng.out.counters.cpu().numpy()]))
+    tok = wl.total_tokens() * wl.L
+    print(json.dumps({"metric": METRIC, "value": round(wl.B / (ms / 1e3), 2), "unit": "scans/s", "n_gpus": 1,
+                      "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+                      "higher_is_better": True, "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+                      "config": {"workload": "one_layer: 16 requests x 1 layer, 32q/8kv heads, d128, bf16 K/V, "
+                                             "page 16, contexts log-uniform 512-8192, summaries from 256 decode "
+                                             "queries", "tokens": wl.total_tokens(), "seed": 2001},
+                      "tokens_scanned_per_s": round(tok / (ms / 1e3), 1),
+                      "summary_update_ms_per_query": round(ema_ms, 4),
+                      "decisions": {"grow": int(c["grows"]), "compact": int(c["compacts"])},
+                      "counters": c}), flush=True)
 
 
 def placements(args):
