@@ -577,14 +577,15 @@ def overlap(args):
     128 requests x 36 layers from 1024-token prompts, page 16.  Two schedules over the
     same steps and the same decisions: serial (the step's boundary batch after its
     attention, one stream; HIP events split the time into decode work and engine work)
-    and overlapped (the boundary requests' attention first, then their boundary batch on
-    a second stream while the other requests' attention runs; the next step waits for
-    it).  The query rows of each subset are gathered by torch before the attention."""
+    and overlapped (engine.OverlapSchedule: the boundary requests' attention first, then
+    their boundary batch on a second stream while the other requests' attention runs;
+    the next step waits for it).  The query rows of each subset are gathered by torch
+    before the attention."""
     import numpy as np
     import torch
 
     from demand_paged_kv_amd import binding as Bd
-    from demand_paged_kv_amd.engine import BoundaryEngine
+    from demand_paged_kv_amd.engine import BoundaryEngine, OverlapSchedule
     from synth.decode_loop import DecodeLoopGen, DecodeSpec
 
     Bd.load()
@@ -600,14 +601,12 @@ def overlap(args):
         pos0 = torch.from_numpy((spec.prompt + gen.fill0).astype(np.int32)).cuda()
         req = torch.arange(spec.B, dtype=torch.int32, device="cuda")
         out = torch.empty((spec.B, spec.L, spec.Hq, spec.d), dtype=torch.float32, device="cuda")
-        side = torch.cuda.Stream()
-        main = torch.cuda.current_stream()
-        done = torch.cuda.Event()
+        sched = OverlapSchedule(eng)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         marks = []
         grows = torch.zeros((), dtype=torch.int64, device="cuda")
-        # boundary / other request ids of every step, built before the loop (they stay alive
-        # to the end, so the second stream never reads memory the allocator handed on)
+        # boundary / other request ids of every step, built before the loop so that building
+        # them is outside the timed region
         ids = []
         for t in range(steps + warm):
             fill += 1
@@ -621,8 +620,6 @@ def overlap(args):
             if t == warm:
                 torch.cuda.synchronize()
                 e0.record()
-            if mode == "overlap":
-                main.wait_event(done)                       # the last boundary batch is complete
             torch.add(pos0, t, out=st.pos)
             bids, oids = ids[t]
             nb = int(bids.numel())
@@ -641,21 +638,8 @@ def overlap(args):
                 if t >= warm:
                     marks.append(m)
             else:
-                eng.update_summaries(q, req)
-                eng.append(k, v, req)
-                if nb:
-                    qb = q[bids.long()]
-                    qo = q[oids.long()]
-                    eng.decode_attention(qb, bids, out[:nb])
-                    ev = torch.cuda.Event()
-                    ev.record(main)
-                    side.wait_event(ev)
-                    eng.step(bids, stream=side)
-                    done.record(side)
-                    eng.decode_attention(qo, oids, out[nb:])
-                else:
-                    eng.decode_attention(q, req, out)
-        main.wait_event(done)
+                sched.step(q, k, v, req, bids, oids, out)
+        sched.finish()
         e1.record()
         torch.cuda.synchronize()
         total = e0.elapsed_time(e1) / steps
@@ -744,13 +728,92 @@ def prefix_share(args):
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(gw, backup, budget):
-    """The oracle, as it stands, on a bounded sample of the same batch (host cores)."""
-    import numpy as np
-    import torch
+def _oracle_worker(conn, start):
+    """One all-cores baseline process: receive a sub-batch, wait for the common start, run
+    the oracle's boundary step on it with one BLAS thread, send back the elapsed time."""
     from threadpoolctl import threadpool_limits
 
     import oracle as O
+    wl, params = conn.recv()
+    conn.send("ready")
+    start.wait()
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.boundary_step(wl, wl.sum_s, wl.sum_l, params)
+        t = time.perf_counter() - t0
+    conn.send(t)
+    conn.close()
+
+
+def _sub_workload(wl, idx):
+    """The requests ``idx`` of a host workload over the same pool state (input plumbing)."""
+    import dataclasses
+    idx = list(idx)
+    return dataclasses.replace(wl, page_table=wl.page_table[idx].copy(), n_alloc=wl.n_alloc[idx].copy(),
+                               fill=wl.fill[idx].copy(), pos=wl.pos[idx].copy(),
+                               k_rows=[wl.k_rows[i] for i in idx], v_rows=[wl.v_rows[i] for i in idx],
+                               sum_s=wl.sum_s[idx], sum_l=wl.sum_l[idx],
+                               regime=None if wl.regime is None else wl.regime[idx].copy())
+
+
+def time_oracle(wl, params, max_workers=16):
+    """Seconds the oracle's boundary step takes on host workload ``wl``: on one thread, and
+    on all cores -- one process per core (at most ``max_workers``; 16 is the GPU machine's CPU
+    share), each running the step on its share of the requests (longest first to the
+    least loaded), all started together after their data has arrived; the all-cores time
+    is the wall time from that start to the last finish.  Returns (t_one, t_all, workers,
+    per-process seconds)."""
+    import multiprocessing as mp
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.boundary_step(wl, wl.sum_s, wl.sum_l, params)
+        t_one = time.perf_counter() - t0
+    nproc = os.cpu_count() or 1
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else nproc
+    workers = max(1, min(max_workers, avail, wl.B))
+    loads = [0] * workers
+    parts = [[] for _ in range(workers)]
+    for i in sorted(range(wl.B), key=lambda i: -int(wl.n(i))):
+        w = int(np.argmin(loads))
+        parts[w].append(i)
+        loads[w] += int(wl.n(i))
+    ctx = mp.get_context("spawn")       # fresh interpreters: the workers never touch the GPU
+    start = ctx.Event()
+    procs, conns = [], []
+    try:
+        for _ in range(workers):
+            a, b = ctx.Pipe()
+            pr = ctx.Process(target=_oracle_worker, args=(b, start), daemon=True)
+            pr.start()
+            procs.append(pr)
+            conns.append(a)
+        for a, part in zip(conns, parts):
+            a.send((_sub_workload(wl, sorted(part)), params))
+        for a in conns:
+            assert a.recv() == "ready"
+        t0 = time.perf_counter()
+        start.set()
+        per = [a.recv() for a in conns]
+        t_all = time.perf_counter() - t0
+    finally:
+        for pr in procs:
+            pr.join(timeout=60)
+            if pr.is_alive():
+                pr.kill()
+    return t_one, t_all, workers, per
+
+
+def cpu_baseline(gw, backup, budget):
+    """The oracle, as it stands, on a bounded sample of the same batch (host cores), on one
+    thread and on all cores (time_oracle)."""
+    import torch
+
     from synth import gpu_workloads as GW
 
     backup.restore()
@@ -762,15 +825,16 @@ def cpu_baseline(gw, backup, budget):
         if acc >= budget:
             break
     wl = GW.to_host_workload(gw, sample)
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        O.boundary_step(wl, wl.sum_s, wl.sum_l, gw.params)
-        t = time.perf_counter() - t0
-    log(f"cpu baseline: {len(sample)} requests, {acc} layer-tokens in {t:.1f}s")
-    return {"value": round(len(sample) / t, 4), "unit": "scans/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {len(sample)} requests of the same batch ({acc} layer-tokens, all 32 layers), "
-                      f"full boundary step (scan, decide, keep-sets, compaction) in float64 numpy, 1 thread",
-            "seconds": round(t, 2), "tokens_scanned_per_s": round(acc / t, 1)}
+    t1, tn, workers, per = time_oracle(wl, gw.params)
+    log(f"cpu baseline: {len(sample)} requests, {acc} layer-tokens: 1 thread {t1:.1f}s; "
+        f"{workers} processes {tn:.1f}s wall (per process {min(per):.1f}-{max(per):.1f}s)")
+    desc = (f"first {len(sample)} requests of the same batch ({acc} layer-tokens, all 32 layers), full "
+            f"boundary step (scan, decide, keep-sets, compaction) in float64 numpy")
+    return {"value": round(len(sample) / tn, 4), "unit": "scans/s", "cores": workers, "kind": "oracle",
+            "sample": desc + f"; {workers} processes over requests, one BLAS thread each",
+            "seconds": round(tn, 2), "tokens_scanned_per_s": round(acc / tn, 1), "nproc": os.cpu_count(),
+            "single_thread": {"value": round(len(sample) / t1, 4), "unit": "scans/s", "cores": 1,
+                              "seconds": round(t1, 2), "tokens_scanned_per_s": round(acc / t1, 1)}}
 
 
 if __name__ == "__main__":

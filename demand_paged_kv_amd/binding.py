@@ -26,7 +26,7 @@ EXPORTED = ("gp_abi_version", "gp_status_string", "gp_last_hip_error_string", "g
             "gp_scratch_bytes",
             "gp_boundary_scan", "gp_decide", "gp_decide_policy", "gp_compact", "gp_compact_prepare",
             "gp_compact_move", "gp_append_kv", "gp_decode_attention", "gp_contiguous_malloc",
-            "gp_contiguous_free")
+            "gp_contiguous_free", "gp_scan_logits")
 # decision policies (gp_decide_policy)
 POLICIES = {"growpage": 0, "random": 1, "inverse": 2, "always_compact": 3, "shrink": 4}
 
@@ -84,6 +84,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gp_boundary_scan.restype = i32
     lib.gp_boundary_scan.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Pages), P, i32, P, P, P, P,
                                      i32, P, ctypes.POINTER(Params), P, P, P, sz, i64, P]
+    lib.gp_scan_logits.restype = i32
+    lib.gp_scan_logits.argtypes = [ctypes.POINTER(KV), i32, i64, P, sz, i32, i32, P, P]
     lib.gp_decide.restype = i32
     lib.gp_decide.argtypes = [P, P, i32, i32, i32, i32, ctypes.POINTER(Params),
                               ctypes.POINTER(Pages), P, P, P, P, P]
@@ -182,6 +184,12 @@ def boundary_scan(kv: KV, pages: Pages, req_ids, n_req, sum_s, sum_l, rope_cos, 
                                  _ptr(stats_out), _ptr(scratch), int(scratch_nbytes),
                                  int(max_total_tokens), _stream(stream))
     _check(st, "gp_boundary_scan")
+
+
+def scan_logits(kv: KV, n_req, max_total_tokens, scratch, scratch_nbytes, entry, n, logits_out, stream=None):
+    st = load().gp_scan_logits(ctypes.byref(kv), int(n_req), int(max_total_tokens), _ptr(scratch),
+                               int(scratch_nbytes), int(entry), int(n), _ptr(logits_out), _stream(stream))
+    _check(st, "gp_scan_logits")
 
 
 def decide(ws, req_ids, n_req, L, Hq, P, prm: Params, pages: Pages, decision_out, delta_out,

@@ -134,6 +134,7 @@ gp_status gp_boundary_scan(const gp_kv* kv, const gp_pages* pages, const int32_t
   if (!req_ids || !sum_s || !sum_l || !ws_out || !scratch) return GP_ERR_INVALID;
   if ((rope_cos == nullptr) != (rope_sin == nullptr)) return GP_ERR_INVALID;
   if (rope_cos && (!pos || rope_max_pos <= 0)) return GP_ERR_INVALID;
+  if ((int64_t)pages->max_pages * kv->P > kMaxSlots) return GP_ERR_UNSUPPORTED;
   if (!aligned(scratch, 256)) return GP_ERR_INVALID;
   const ScratchLayout lay = scratch_layout(*kv, n_req, max_total_tokens);
   if (scratch_bytes < lay.total) return GP_ERR_SCRATCH;
@@ -141,6 +142,22 @@ gp_status gp_boundary_scan(const gp_kv* kv, const gp_pages* pages, const int32_t
   return from_hip(launch_scan(g, scratch_ptrs(scratch, lay), max_total_tokens, sum_s, sum_l, rope_cos,
                               rope_sin, rope_max_pos, pos, params->top_p, params->n_local,
                               params->shrink, ws_out, stats_out, (hipStream_t)stream));
+}
+
+gp_status gp_scan_logits(const gp_kv* kv, int32_t n_req, int64_t max_total_tokens, const void* scratch,
+                         size_t scratch_bytes, int32_t entry, int32_t n, float* logits_out, void* stream) {
+  if (!kv || kv->L <= 0 || kv->Hkv <= 0 || kv->Hq <= 0 || kv->P <= 0) return GP_ERR_INVALID;
+  if (n_req <= 0 || entry < 0 || entry >= n_req || n < 0 || max_total_tokens < 0) return GP_ERR_INVALID;
+  if (!scratch || !aligned(scratch, 256)) return GP_ERR_INVALID;
+  if (n == 0) return GP_OK;
+  if (!logits_out) return GP_ERR_INVALID;
+  const ScratchLayout lay = scratch_layout(*kv, n_req, max_total_tokens);
+  if (scratch_bytes < lay.total) return GP_ERR_SCRATCH;
+  Geo g{};
+  g.L = kv->L;
+  g.Hkv = kv->Hkv;
+  return from_hip(launch_copy_logits(g, scratch_ptrs(const_cast<void*>(scratch), lay), entry, n, logits_out,
+                                     (hipStream_t)stream));
 }
 
 gp_status gp_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_req, int32_t L,

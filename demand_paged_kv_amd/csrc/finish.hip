@@ -18,7 +18,8 @@
 //           element of bin b carries at least the mass of x = (b+1)/16); in the same
 //           pass the slot importance max_k exp(l_k - M_k) / Z_k feeds a threshold
 //           buffer that keeps the n - k least important candidate slots (ties: older
-//           slot first) -- the slots a compaction evicts; whenever the buffer fills, a
+//           slot first; importance ranked in the log domain, float64) -- the slots a
+//           compaction evicts; whenever the buffer fills, a
 //           radix select keeps its n - k smallest keys and lowers the threshold.
 //   refine  per row, an exact radix select over the b* elements only, weighted by the
 //           same fixed-point masses, in digits of 8 bits from the highest key bit in
@@ -119,6 +120,18 @@ __device__ __forceinline__ int finish_w(uint32_t prefix, float M, u64 T, u64 acc
   const u64 need = T > acc_mass ? T - acc_mass : 0;
   const u64 jn = q ? (need + q - 1) / q : 1ull;
   return (int)min((u64)n, (u64)acc_cnt + max(jn, 1ull));
+}
+
+// Keep-set key of slot i with negative log-importance v >= 0: bits 62..24 hold the top 39
+// bits of v's float64 pattern complemented (a less important slot has a smaller key; the
+// sign bit, always 0, is dropped, so every key stays below the buffer's initial
+// threshold of all ones), the low 24 bits the slot, so that equal importance evicts the
+// older slot first.  Relative resolution 2^-27; slots stay below 2^24 (max_pages * P is
+// checked on the host).
+constexpr u64 kSlotMask = (1ull << 24) - 1ull;
+__device__ __forceinline__ u64 imp_key(double v, int i) {
+  const u64 vb = (u64)__double_as_longlong(v);
+  return (((~vb) << 1) >> 25 << 24) | (u64)(uint32_t)i;
 }
 
 // Exact weighted radix select by one wave over the m LDS elements of one row (keys
@@ -353,7 +366,8 @@ __device__ __forceinline__ void finish_unit(const FinishArgs& a, int rank, int l
   u64 (*ms)[256] = lds.ms;
   float* cand = lds.cand;
   u64* kbuf = lds.kbuf;
-  __shared__ float s_M[kDists], s_iz[kDists];
+  __shared__ float s_M[kDists];
+  __shared__ double s_lse[kDists];
   __shared__ u64 s_T[kDists], s_above[kDists], s_Z[kDists];
   __shared__ uint32_t s_above_cnt[kDists], s_red[8];
   __shared__ int s_mode[kDists], s_bin[kDists], s_off[kDists], s_fill[kDists], s_ub[kDists], s_W[kDists];
@@ -508,15 +522,15 @@ __device__ __forceinline__ void finish_unit(const FinishArgs& a, int rank, int l
     s_kcount = 0;
     s_ktau = ~0ull;
   }
-  if (tid < kDists) {
+  if (tid < kDists) {  // log of the softmax normaliser: ln(sum exp(l)) = M + ln Z
     const double z = (double)s_Z[tid] / (double)kMassScale;
-    s_iz[tid] = (float)(1.0 / z);
+    s_lse[tid] = (double)s_M[tid] + log(z);
   }
   __syncthreads();
 
   // ---- read 2: counts above the crossing bins, crossing-bin elements, keep-set candidates
   int mode[kDists], binstar[kDists], boff[kDists], bub[kDists];
-  float iz[kDists];
+  double lse[kDists];
   uint32_t above[kDists];
 #pragma unroll
   for (int k = 0; k < kDists; ++k) {
@@ -524,7 +538,7 @@ __device__ __forceinline__ void finish_unit(const FinishArgs& a, int rank, int l
     binstar[k] = s_bin[k];
     boff[k] = s_off[k];
     bub[k] = s_ub[k];
-    iz[k] = s_iz[k];
+    lse[k] = s_lse[k];
     above[k] = 0;
   }
   float4 nlo = make_float4(0.f, 0.f, 0.f, 0.f), nhi = nlo;
@@ -540,7 +554,10 @@ __device__ __forceinline__ void finish_unit(const FinishArgs& a, int rank, int l
       nhi = *reinterpret_cast<const float4*>(x + (int64_t)(i + 256) * kDists + 4);
     }
     if (i < n) {
-      float imp = 0.f;  // slot importance: max over rows of exp(l - M) / Z
+      // slot importance max over rows of exp(l - M) / Z, ranked by its negative log
+      // nl = min over rows of (M + ln Z - l) >= 0 in float64: no underflow however far
+      // below the maximum a slot lies, and no rounding beyond the logits' own
+      double nl = INFINITY;
 #pragma unroll
       for (int k = 0; k < kDists; ++k) {
         const float v = v8[k];
@@ -551,10 +568,10 @@ __device__ __forceinline__ void finish_unit(const FinishArgs& a, int rank, int l
           const int p = atomicAdd(&s_fill[k], 1);
           if (mode[k] == MODE_LDS && p < bub[k]) cand[boff[k] + p] = v;  // beyond the bound: block path
         }
-        imp = fmaxf(imp, exp2f(-xv * kLog2e) * iz[k]);  // keeps tiny results (denormals) ordered
+        nl = fmin(nl, lse[k] - (double)v);
       }
       if (E > 0 && i < cand_slots) {
-        const u64 key = ((u64)__float_as_uint(imp) << 32) | (uint32_t)i;
+        const u64 key = imp_key(nl, i);
         if (key < s_ktau) kbuf[atomicAdd(&s_kcount, 1)] = key;
       }
     }
@@ -589,7 +606,7 @@ __device__ __forceinline__ void finish_unit(const FinishArgs& a, int rank, int l
     if (tid == 0) s_c2 = 0;
     __syncthreads();
     for (int j = tid; j < cnt; j += 256)
-      if (kbuf[j] <= K) sel[atomicAdd(&s_c2, 1)] = (uint32_t)(kbuf[j] & 0xffffffffu);
+      if (kbuf[j] <= K) sel[atomicAdd(&s_c2, 1)] = (uint32_t)(kbuf[j] & kSlotMask);
     __syncthreads();
     for (int t = tid; t < E; t += 256) {  // E <= 2P <= 512
       const uint32_t s = sel[t];

@@ -12,6 +12,7 @@ namespace gp {
 constexpr int kDists = 8;          // 4 query heads per KV head x 2 summaries
 constexpr int kGroup = 4;          // query heads per KV head
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int64_t kMaxSlots = 1 << 24;  // candidate slots per request (max_pages * P) the scan indexes
 constexpr int kReqFields = 8;      // per-request int32 fields of the compaction plan
 constexpr int kLogitAlign = 16;    // each unit's logit rows start on a 512-byte boundary
 
@@ -138,6 +139,9 @@ hipError_t launch_scan(const Geo& g, const ScratchPtrs& sp, int64_t max_tokens,
                        const float* rope_sin, int32_t rope_max_pos, const int32_t* pos,
                        float top_p, int32_t n_local, int32_t shrink, int32_t* ws_out,
                        float* stats_out, hipStream_t st);
+
+hipError_t launch_copy_logits(const Geo& g, const ScratchPtrs& sp, int32_t entry, int32_t n, float* out,
+                              hipStream_t st);
 
 struct FinishArgs {
   Geo g;

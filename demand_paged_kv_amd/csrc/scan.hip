@@ -305,4 +305,25 @@ hipError_t launch_scan(const Geo& g, const ScratchPtrs& sp, int64_t max_tokens,
   return launch_finish(f, st);
 }
 
+// ----------------------------------------------------------------------------- logit read-back
+// Copy of batch entry `entry`'s logits from the scratch of the last scan: block u = l *
+// Hkv + g writes out[l][g][t][8] for t < n (NaN where the scan held no row: t >= the
+// entry's candidate count, or an entry over the token budget).
+__global__ __launch_bounds__(256) void copy_logits_kernel(ScratchPtrs sp, int32_t L, int32_t Hkv, int32_t entry,
+                                                          int32_t n, float* out) {
+  const int u = blockIdx.x;
+  const int nt = sp.flags[entry] ? 0 : sp.n_tok[entry];
+  const float* src = sp.logits + (sp.tok_off[entry] * L * Hkv + (int64_t)u * logit_rows(nt)) * kDists;
+  float* dst = out + (int64_t)u * n * kDists;
+  for (int64_t i = threadIdx.x; i < (int64_t)n * kDists; i += 256)
+    dst[i] = i < (int64_t)nt * kDists ? src[i] : __builtin_nanf("");
+}
+
+hipError_t launch_copy_logits(const Geo& g, const ScratchPtrs& sp, int32_t entry, int32_t n, float* out,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(copy_logits_kernel, dim3((unsigned)(g.L * g.Hkv)), dim3(256), 0, st, sp, g.L, g.Hkv, entry,
+                     n, out);
+  return hipGetLastError();
+}
+
 }  // namespace gp

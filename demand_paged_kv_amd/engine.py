@@ -61,11 +61,29 @@ class StepOutputs:
     counters: torch.Tensor    # [GP_NUM_COUNTERS] int32
 
 
+def _as_stream(stream):
+    """``stream`` as a torch stream object (None: the current stream)."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream) if stream else torch.cuda.default_stream()
+    return stream
+
+
 class BoundaryEngine:
     """Runs scan -> decide -> compact for batches of requests on one device state.
 
     Output and scratch buffers are allocated once for a maximum batch and token count
     and reused, so a step launches kernels only.
+
+    Lifetimes.  Every call is asynchronous: the kernels read and write the tensors they
+    are given after the call has returned.  When a method runs on a ``stream`` other
+    than the current one, it marks every tensor of the launch -- the caller's (request
+    ids, queries, rows, outputs, draws) and the engine's and state's own -- as used on
+    that stream (``Tensor.record_stream``), so torch's caching allocator does not hand
+    their memory to other work before that stream's queued work is done, even if Python
+    drops them right after the call.  On the current stream the allocator's own stream
+    order gives the same guarantee.
     """
 
     def __init__(self, st: DeviceState, max_batch: int, max_total_tokens: int, prm: B.Params):
@@ -92,6 +110,22 @@ class BoundaryEngine:
         self.policy, self.rand_u, self.grow_prob = ("shrink" if prm.shrink else "growpage"), None, 0.0
         self._view_evicted()
 
+    def _tie(self, stream, *tensors):
+        """Mark the launch's tensors (plus the engine's and the state's) as used on a
+        stream other than the current one (see the class docstring)."""
+        if stream is None:
+            return
+        s = _as_stream(stream)
+        if s == torch.cuda.current_stream():
+            return
+        st, o = self.st, self.out
+        own = (st.k_pool, st.v_pool, st.page_table, st.n_alloc, st.fill, st.refcount, st.free_stack,
+               st.free_top, st.sum_s, st.sum_l, st.pos, st.rope_cos, st.rope_sin, self.scratch, o.ws,
+               o.stats, o.decision, o.delta, o.status, o.counters, self._ev_store, self.rand_u)
+        for t in own + tensors:
+            if t is not None and t.is_cuda:
+                t.record_stream(s)
+
     def _view_evicted(self):
         """Evicted-slot rows are P wide, 2P under SHRINK (gp_compact's evicted_out)."""
         st, n = self.st, self.max_batch
@@ -105,6 +139,18 @@ class BoundaryEngine:
                         st.rope_sin, max_pos, st.pos if st.rope_cos is not None else None, self.prm,
                         o.ws, o.stats, self.scratch, self.scratch_nbytes, self.max_total_tokens,
                         stream)
+        self._tie(stream, req_ids)
+        self._scan_batch = nb
+
+    def scan_logits(self, entry: int, n: int, stream=None) -> torch.Tensor:
+        """The last scan's logits of batch entry ``entry`` (n candidate slots) as a new
+        [L][Hkv][n][8] float32 tensor, row 2*j + s = query head 4g + j, summary s."""
+        st = self.st
+        out = torch.empty((st.L, st.Hkv, int(n), 8), dtype=torch.float32, device=st.k_pool.device)
+        B.scan_logits(self.kv, self._scan_batch, self.max_total_tokens, self.scratch, self.scratch_nbytes,
+                      int(entry), int(n), out, stream)
+        self._tie(stream, out)
+        return out
 
     def decide(self, req_ids: torch.Tensor, stream=None):
         st, o, nb = self.st, self.out, int(req_ids.numel())
@@ -115,6 +161,7 @@ class BoundaryEngine:
             B.decide_policy(o.ws, req_ids, nb, st.L, st.Hq, st.P, self.prm, self.policy, self.rand_u,
                             self.grow_prob, self.pages, o.decision, o.delta, o.status, o.counters,
                             stream)
+        self._tie(stream, req_ids)
 
     def set_policy(self, policy: str = "growpage", rand_u: Optional[torch.Tensor] = None,
                    grow_prob: float = 0.0):
@@ -130,16 +177,19 @@ class BoundaryEngine:
         o, nb = self.out, int(req_ids.numel())
         B.compact(self.kv, self.pages, req_ids, o.decision, nb, self.prm, o.evicted, o.status,
                   o.counters, self.scratch, self.scratch_nbytes, self.max_total_tokens, stream)
+        self._tie(stream, req_ids)
 
     def compact_prepare(self, req_ids: torch.Tensor, stream=None):
         o, nb = self.out, int(req_ids.numel())
         B.compact_prepare(self.kv, self.pages, req_ids, o.decision, nb, self.prm, o.evicted, o.status,
                           self.scratch, self.scratch_nbytes, self.max_total_tokens, stream)
+        self._tie(stream, req_ids)
 
     def compact_move(self, req_ids: torch.Tensor, stream=None):
         nb = int(req_ids.numel())
         B.compact_move(self.kv, self.pages, req_ids, nb, self.out.counters, self.scratch,
                        self.scratch_nbytes, self.max_total_tokens, stream)
+        self._tie(stream, req_ids)
 
     def step(self, req_ids: torch.Tensor, stream=None) -> StepOutputs:
         """One boundary batch: scan, decide (+grow), compact.  Asynchronous."""
@@ -157,6 +207,7 @@ class BoundaryEngine:
         B.update_summaries(q, qd, (q.stride(0), q.stride(1), q.stride(2)), req_ids,
                            int(req_ids.numel()), st.L, st.Hq, st.d, st.sum_s, st.sum_l, self.prm,
                            stream)
+        self._tie(stream, q, req_ids)
 
     def append(self, k_new: torch.Tensor, v_new: torch.Tensor, req_ids: torch.Tensor,
                status_out: Optional[torch.Tensor] = None, stream=None):
@@ -164,6 +215,7 @@ class BoundaryEngine:
         assert k_new.is_contiguous() and v_new.is_contiguous()
         B.append_kv(self.kv, self.pages, k_new, v_new, req_ids, int(req_ids.numel()), status_out,
                     stream)
+        self._tie(stream, k_new, v_new, req_ids, status_out)
 
     def decode_attention(self, q: torch.Tensor, req_ids: torch.Tensor, out: torch.Tensor, stream=None):
         """out[b][l][h] = attention of q[b][l][h] (pre-RoPE, rotated to st.pos) over the
@@ -175,6 +227,7 @@ class BoundaryEngine:
         B.decode_attention(self.kv, self.pages, q, qd, (q.stride(0), q.stride(1), q.stride(2)), req_ids,
                            int(req_ids.numel()), st.rope_cos, st.rope_sin, max_pos,
                            st.pos if st.rope_cos is not None else None, out, stream)
+        self._tie(stream, q, req_ids, out)
 
     def decode_step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                     req_ids: torch.Tensor, boundary_ids: Optional[torch.Tensor] = None,
@@ -225,3 +278,58 @@ class DecodeGraph:
         boundary batch, None otherwise."""
         (self.boundary if boundary else self.plain).replay()
         return self.eng.out if boundary else None
+
+
+class OverlapSchedule:
+    """A decode step with the boundary batch on a second stream, beside the other requests'
+    decode attention (the background compression the pages keep from Zipage: GrowPage
+    review, FAQ "How does GrowPage differ from Zipage?").
+
+    Per step, on the current stream: the summaries absorb q and the K/V rows are appended
+    for every request (after the previous step's boundary batch has finished); then the
+    attention of the requests at a boundary (``bids``) runs first, over their pages as
+    they stand; the boundary batch of those requests is queued on the side stream, and
+    the attention of the other requests (``oids``) runs on the current stream at the same
+    time.  Requests at a boundary and the others touch disjoint pages (a shared page is
+    never changed in place), so the two streams do not race; the next step waits for the
+    side stream.  Attention outputs go to ``out`` in the order (bids, oids): row i holds
+    request ``order[i]``.  The result equals the serial schedule's (attention of every
+    request, then the boundary batch) bit for bit.  Request-id tensors may be
+    temporaries: the engine ties every tensor it launches on the side stream to it."""
+
+    def __init__(self, eng: "BoundaryEngine", side: Optional[torch.cuda.Stream] = None):
+        self.eng = eng
+        self.side = side if side is not None else torch.cuda.Stream()
+        self.done = torch.cuda.Event()
+        self.pending = False
+
+    def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, req_ids: torch.Tensor,
+             bids: torch.Tensor, oids: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+        """One decode step (see the class docstring); ``q``, ``k_new``, ``v_new`` are
+        indexed like ``req_ids`` (request slot == batch position); returns ``order``."""
+        eng = self.eng
+        main = torch.cuda.current_stream()
+        if self.pending:
+            main.wait_event(self.done)
+        eng.update_summaries(q, req_ids)
+        eng.append(k_new, v_new, req_ids)
+        nb = int(bids.numel())
+        if nb == 0:
+            eng.decode_attention(q, req_ids, out)
+            self.pending = False
+            return req_ids
+        eng.decode_attention(q[bids.long()], bids, out[:nb])
+        ready = torch.cuda.Event()
+        ready.record(main)
+        self.side.wait_event(ready)
+        eng.step(bids, stream=self.side)
+        self.done.record(self.side)
+        self.pending = True
+        eng.decode_attention(q[oids.long()], oids, out[nb:])
+        return torch.cat([bids, oids])
+
+    def finish(self):
+        """Make the current stream wait for the last boundary batch."""
+        if self.pending:
+            torch.cuda.current_stream().wait_event(self.done)
+            self.pending = False

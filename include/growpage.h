@@ -19,6 +19,14 @@
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
  *     Nothing is synchronised with the host; device-side outcomes (pool exhaustion,
  *     copy-on-write shortfall) are reported per request in `status_out`.
+ *   - Lifetimes: the library keeps no reference to a buffer once a call returns, but the
+ *     kernels it queued read and write every buffer passed (request ids, inputs, outputs,
+ *     scratch, pools, page state) until they complete.  Each buffer must stay allocated,
+ *     and must not be handed to other work, until the work queued on `stream` is done:
+ *     order its release after that stream (an event recorded on it, or a stream-aware
+ *     allocator told of the use, e.g. PyTorch's Tensor.record_stream).  Releasing a
+ *     request-id array right after a call on a second stream lets an allocator reuse it
+ *     while the kernels still index page tables with it.
  *   - Argument errors are detected on the host before any launch and return
  *     GP_ERR_INVALID (nothing is launched).  A failed launch returns GP_ERR_HIP.
  *     Shapes the kernels do not implement return GP_ERR_UNSUPPORTED.
@@ -170,13 +178,25 @@ size_t gp_scratch_bytes(const gp_kv* kv, int32_t n_req, int64_t max_total_tokens
  * statistics are also kept in `scratch` for gp_compact, so the same scratch must be
  * passed to gp_compact unchanged.  The page state is only read.
  * Errors: GP_ERR_INVALID (NULL/shape), GP_ERR_SCRATCH (scratch too small),
- * GP_ERR_UNSUPPORTED (Hq != 4*Hkv, d not 64/128, P % 8 != 0). */
+ * GP_ERR_UNSUPPORTED (Hq != 4*Hkv, d not 64/128, P % 8 != 0, max_pages * P > 2^24). */
 gp_status gp_boundary_scan(const gp_kv* kv, const gp_pages* pages, const int32_t* req_ids,
                            int32_t n_req, const float* sum_s, const float* sum_l,
                            const float* rope_cos, const float* rope_sin, int32_t rope_max_pos,
                            const int32_t* pos, const gp_params* params, int32_t* ws_out,
                            float* stats_out, void* scratch, size_t scratch_bytes,
                            int64_t max_total_tokens, void* stream);
+
+/* The logits behind the last gp_boundary_scan's working sets (GrowPage review, "Summary":
+ * each summary is scored against every retained key), for inspection and parity checks:
+ * copies batch entry `entry`'s scores from `scratch` (the scan's, unchanged since; n_req
+ * and max_total_tokens as passed to it) to logits_out [L][Hkv][n][8] float32, row
+ * 2*j + s being query head g*4 + j of KV head g under summary s (0 short, 1 long),
+ * scaled by 1/sqrt(d) and rotated as the scan did.  n: the entry's candidate slots
+ * n_alloc*P + fill; slots the scan did not score (t >= its count, or an entry flagged
+ * GP_REQ_OVERFLOW) read NaN.  gp_compact leaves the scores in place.
+ * Errors: GP_ERR_INVALID (NULL, entry outside [0, n_req), n < 0), GP_ERR_SCRATCH. */
+gp_status gp_scan_logits(const gp_kv* kv, int32_t n_req, int64_t max_total_tokens, const void* scratch,
+                         size_t scratch_bytes, int32_t entry, int32_t n, float* logits_out, void* stream);
 
 /* Decision and grow (GrowPage review, "Summary": one more page when the fast summary's
  * working set is the larger; FAQ: tau).  delta_out[b] = sum over l, h of

@@ -306,11 +306,12 @@ def direct_case(seed: int, B: int = 4, L: int = 2, Hq: int = 8, Hkv: int = 2, d:
 
 def planted_logits_case(seed: int, logit_fns, L: int = 1, Hq: int = 8, Hkv: int = 2, d: int = 64,
                         P: int = 16, params: Optional[dict] = None, spare_pages: int = 8,
-                        name: str = "planted") -> Workload:
+                        name: str = "planted", dtype: str = "f32") -> Workload:
     """Requests whose scores are planted exactly: every summary (all heads, both
     timescales) is the unit vector e_0 and key i carries logit_fn(rng, n)[i] * sqrt(d) in
-    component 0 (float32 storage, no RoPE), so each softmax row sees those logits.  Both
-    summaries coincide, so every request compacts.  ``logit_fns[b]`` = (n_alloc, fn)."""
+    component 0 (float32 storage, or bf16 by round-to-nearest-even; no RoPE), so each
+    softmax row sees those logits (as stored).  Both summaries coincide, so every request
+    compacts.  ``logit_fns[b]`` = (n_alloc, fn)."""
     rng = np.random.default_rng(seed)
     B = len(logit_fns)
     A = np.array([a for a, _ in logit_fns], np.int32)
@@ -324,10 +325,10 @@ def planted_logits_case(seed: int, logit_fns, L: int = 1, Hq: int = 8, Hkv: int 
         lg = np.asarray(fn(rng, int(n[b])), np.float64)
         kb = rng.standard_normal((L, Hkv, int(n[b]), d))
         kb[..., 0] = lg * math.sqrt(d)
-        k_rows.append(kb.astype(np.float32))
-        v_rows.append(rng.standard_normal((L, Hkv, int(n[b]), d)).astype(np.float32))
+        k_rows.append(_storage(kb, dtype))
+        v_rows.append(_storage(rng.standard_normal((L, Hkv, int(n[b]), d)), dtype))
     e0 = np.zeros((B, L, Hq, d), np.float32)
     e0[..., 0] = 1.0
-    return Workload(name, L, Hq, Hkv, d, P, "f32", num_pages, max_pages, table, A, fill,
+    return Workload(name, L, Hq, Hkv, d, P, dtype, num_pages, max_pages, table, A, fill,
                     n.astype(np.int32), rc, stack, top, k_rows, v_rows, e0, e0.copy(), None, "f32",
                     None, None, dict(params or PARAMS_DEFAULT), seed, regime=np.zeros(B, np.int32))

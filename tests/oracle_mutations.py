@@ -54,6 +54,17 @@ MUTATIONS = {
                                 "softmax_stats(logits(qt[None, :], kf) * math.sqrt(d))"),
     "attention_query_not_rotated": ("decode_attention", "qt = rope_rotate(qf[l, h], cos_row, sin_row)",
                                     "qt = qf[l, h]"),
+    "query_bf16_misaligned": ("query_f32", "astype(np.uint32) << 16)", "astype(np.uint32) << 15)"),
+    "widen_bf16_misaligned": ("widen", "astype(np.uint32) << 16)", "astype(np.uint32) << 15)"),
+    "query_bf16_as_float16": ("query_f32", "return (np.asarray(q, np.uint16).astype(np.uint32) << 16).view(np.float32)",
+                              "return np.asarray(q, np.uint16).view(np.float16).astype(np.float32)"),
+    "delta_range_point_bounds": ("delta_range",
+                                 "lo = int(np.sum(Wlo[..., 0] - Whi[..., 1]))\n    hi = int(np.sum(Whi[..., 0] - Wlo[..., 1]))",
+                                 "lo = d\n    hi = d"),
+    "delta_range_same_side": ("delta_range", "lo = int(np.sum(Wlo[..., 0] - Whi[..., 1]))",
+                              "lo = int(np.sum(Wlo[..., 0] - Wlo[..., 1]))"),
+    "importance_in_float32": ("importance", "np.asarray(a_group, np.float64).max(axis=0)",
+                              "np.asarray(a_group, np.float32).max(axis=0).astype(np.float64)"),
 }
 
 

@@ -414,3 +414,49 @@ def check_pool_shared(st, before: dict, out, n_req: int, P: int, tau: int, shrin
     assert np.array_equal(refs, g_rc), "refcount != references"
     return dict(grows=int((want_dec == 1).sum()), denied=int(((want_status & O.REQ_GROW_DENIED) != 0).sum()),
                 deferred=int(((want_status & O.REQ_DEFERRED) != 0).sum()), freed=len(freed))
+
+
+PROB_RTOL = 1e-3
+
+
+def compare_logits(eng, wl, entries, host_idx=None):
+    """Element-wise float parity of the scan: for batch entries ``entries`` (host requests
+    ``host_idx``, default the same indices of ``wl``), every logit the kernels produced
+    (read back from the scan's scratch) against the oracle's float64 logits within
+    ``LOGIT_TOL`` (absolute, relative above 1), and every softmax probability -- the
+    GPU's logit with the GPU's own max and sum-exp, exp(l - M) / Z -- against the
+    oracle's within relative ``PROB_RTOL``.  The GPU's max must also be the max of its
+    own logits (bit for bit).  Returns (max logit error, max probability error)."""
+    host_idx = list(entries) if host_idx is None else list(host_idx)
+    stats = eng.out.stats.cpu().numpy()
+    G = wl.Hq // wl.Hkv
+    worst_l = worst_p = 0.0
+    for b, i in zip(entries, host_idx):
+        n = wl.n(i)
+        if n == 0:          # no scores (reading R17); the statistics are checked elsewhere
+            continue
+        lg_gpu = eng.scan_logits(int(b), n).cpu().numpy().astype(np.float64)   # [L][Hkv][n][8]
+        assert not np.isnan(lg_gpu).any(), ("unscored slot", b)
+        cr = sr = None
+        if wl.rope_cos is not None:
+            cr, sr = wl.rope_cos[wl.pos[i]], wl.rope_sin[wl.pos[i]]
+        for l in range(wl.L):
+            for g in range(wl.Hkv):
+                kf = O.widen(wl.k_rows[i][l, g], wl.dtype)
+                for j in range(G):
+                    h = g * G + j
+                    for sig, summ in enumerate((wl.sum_s, wl.sum_l)):
+                        qt = O.rope_rotate(summ[i][l, h], cr, sr)
+                        ref = O.logits(qt[None, :], kf)[0]
+                        M_ref, Z_ref, a_ref = O.softmax_stats(ref[None])
+                        got = lg_gpu[l, g, :, 2 * j + sig]
+                        err = np.abs(got - ref) / np.maximum(1.0, np.abs(ref))
+                        worst_l = max(worst_l, float(err.max()))
+                        M_gpu, Z_gpu = stats[b, l, h, sig]
+                        assert np.float32(M_gpu) == np.float32(got.max()), (b, l, h, sig, M_gpu, got.max())
+                        a_gpu = np.exp(got - np.float64(M_gpu)) / np.float64(Z_gpu)
+                        perr = np.abs(a_gpu - a_ref[0]) / a_ref[0]
+                        worst_p = max(worst_p, float(perr.max()))
+    assert worst_l <= LOGIT_TOL, f"logit error {worst_l}"
+    assert worst_p <= PROB_RTOL, f"probability error {worst_p}"
+    return worst_l, worst_p

@@ -112,6 +112,19 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert dp(prm, B.POLICIES["shrink"]) == B.GP_ERR_INVALID
     assert dp(sh, B.POLICIES["growpage"]) == B.GP_ERR_INVALID
     assert dp(prm, 5) == B.GP_ERR_INVALID
+    # more candidate slots per request (max_pages * P) than the keep-set keys index
+    big = B.Pages(0x3000, 4, (1 << 24) // 16 + 1, 0x4000, 0x5000, 0x6000, 0x7000, 0x8000)
+    assert lib.gp_boundary_scan(*args(p=big)) == B.GP_ERR_UNSUPPORTED
+    # logit read-back: entry inside the batch, the scan's scratch size
+    sl = lambda entry=0, n=10, nreq=1, scr=0x10000, nb=1 << 40, out=0xf000: lib.gp_scan_logits(
+        P(kv), nreq, 10, scr, nb, entry, n, out, None)
+    assert sl(entry=1) == B.GP_ERR_INVALID
+    assert sl(entry=-1) == B.GP_ERR_INVALID
+    assert sl(n=-1) == B.GP_ERR_INVALID
+    assert sl(out=None) == B.GP_ERR_INVALID
+    assert sl(scr=0x10010) == B.GP_ERR_INVALID
+    assert sl(nb=16) == B.GP_ERR_SCRATCH
+    assert sl(n=0) == B.GP_OK                                        # nothing to copy: nothing launched
 
 
 def test_param_struct_matches_header():

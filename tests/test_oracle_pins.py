@@ -62,6 +62,79 @@ def test_ema_run_matches_stepwise_and_bias():
     assert abs(float(l_[0, 0]) - (1 - 0.999 ** 32)) < 1e-5
 
 
+# ----------------------------------------------------------------------------- stored values
+# bf16 bit patterns with the values IEEE-754 binary16-brain fixes for them: sign, 8
+# exponent bits (bias 127), 7 fraction bits; exponent 0 is the subnormal range.
+BF16_VALUES = [
+    (0x3F80, 1.0),
+    (0xC000, -2.0),
+    (0x3FC0, 1.5),
+    (0x4049, 3.140625),
+    (0xBF00, -0.5),
+    (0x0001, 2.0 ** -133),                          # smallest subnormal: 2^-126 * 2^-7
+    (0x007F, 127 * 2.0 ** -133),                    # largest subnormal
+    (0x0080, 2.0 ** -126),                          # smallest normal
+    (0x7F7F, (2.0 - 2.0 ** -7) * 2.0 ** 127),       # largest finite
+    (0xFF7F, -(2.0 - 2.0 ** -7) * 2.0 ** 127),
+    (0x0000, 0.0),
+]
+
+
+@pytest.mark.parametrize("fn", ["widen", "query_f32"])
+def test_bf16_bit_patterns_decode_to_their_values(fn):
+    """Stored bf16 keys and values (widen) and bf16 decode queries (query_f32) decode to the
+    values their bit patterns define, subnormals and the extremes included."""
+    bits = np.array([b for b, _ in BF16_VALUES], np.uint16)
+    want = np.array([v for _, v in BF16_VALUES], np.float64)
+    got = getattr(O, fn)(bits, "bf16").astype(np.float64)
+    assert np.array_equal(got, want), (got, want)
+    neg0 = getattr(O, fn)(np.array([0x8000], np.uint16), "bf16")
+    assert neg0[0] == 0.0 and np.signbit(neg0[0])
+    inf = getattr(O, fn)(np.array([0x7F80, 0xFF80], np.uint16), "bf16")
+    assert inf[0] == np.inf and inf[1] == -np.inf
+    assert np.isnan(getattr(O, fn)(np.array([0x7FC0], np.uint16), "bf16")[0])
+
+
+def test_widen_and_query_keep_float32_values():
+    """float32 storage is taken as it is (widen to float64 exactly, queries unchanged)."""
+    x = np.array([1.0, -2.5, 2.0 ** -149, 3.4028234663852886e38, 1.0 + 2.0 ** -23], np.float32)
+    assert np.array_equal(O.widen(x, "f32"), x.astype(np.float64))
+    assert O.widen(x, "f32").dtype == np.float64
+    q = O.query_f32(x, "f32")
+    assert q.dtype == np.float32 and np.array_equal(q.view(np.uint32), x.view(np.uint32))
+
+
+def test_bf16_widening_is_the_top_half_of_float32():
+    """Every bf16 pattern equals the float32 whose upper 16 bits it is (lower bits zero):
+    checked on all 65536 patterns through float32 rounding of the float64 value."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):          # the NaN patterns
+        w = O.widen(bits, "bf16")
+        q = O.query_f32(bits, "bf16")
+    f = w.astype(np.float32)
+    ok = ~np.isnan(w)
+    assert np.array_equal((f.view(np.uint32)[ok] >> 16).astype(np.uint16), bits[ok])
+    assert np.array_equal(f.view(np.uint32)[ok] & 0xFFFF, np.zeros(int(ok.sum()), np.uint32))
+    assert np.array_equal(q.view(np.uint32)[ok], f.view(np.uint32)[ok])
+
+
+@pytest.mark.parametrize("beta", [0.9, 0.999])
+def test_ema_run_constant_bf16_query_closed_form(beta):
+    """A constant bf16 query from zero gives s_t = (1 - beta^t) q for the query's decoded
+    value q (closed form, within the float32 rounding of t steps): pins the bf16 branch
+    of the summaries' input."""
+    bits = np.array([0x3F80, 0xC040, 0x4049, 0x3D4D, 0xBB80], np.uint16)     # 1, -3, 3.140625, ~0.0501, ~-0.0039
+    q = np.array([1.0, -3.0, 3.140625, 0.050048828125, -0.00390625])
+    T = 64
+    queries = np.broadcast_to(bits, (T, bits.size)).copy()
+    s, l_ = O.ema_run(queries, "bf16", beta, 0.5)
+    b = float(np.float32(beta))
+    want = (1.0 - b ** T) * q
+    assert np.all(np.abs(s.astype(np.float64) - want) <= (T + 1) * 2.0 ** -22 * np.abs(q)), (s, want)
+    want_l = (1.0 - 0.5 ** T) * q
+    assert np.all(np.abs(l_.astype(np.float64) - want_l) <= (T + 1) * 2.0 ** -22 * np.abs(q))
+
+
 # ----------------------------------------------------------------------------- RoPE (R4)
 def test_rope_identity_and_quarter_turn():
     rng = np.random.default_rng(4)
@@ -229,6 +302,64 @@ def test_equal_betas_always_compact():
     s, l_ = O.ema_run(wl.queries, wl.q_dtype, 0.9, 0.9)
     res = O.boundary_step(wl, s, l_, wl.params)
     assert res.delta[0] == 0 and res.decision[0] == O.DECISION_COMPACT
+
+
+def test_delta_range_hand_built():
+    """delta = sum(W_S - W_L); the near-tie range pairs each short size's low end with the
+    long size's high end and the other way round (hand-computed integers)."""
+    # [L=2][Hq=2][2]: (short, long)
+    W = np.array([[[5, 3], [7, 4]], [[2, 6], [9, 9]]])
+    Wlo = np.array([[[4, 3], [7, 2]], [[2, 5], [8, 9]]])
+    Whi = np.array([[[6, 3], [9, 5]], [[3, 6], [9, 10]]])
+    d, lo, hi = O.delta_range(W, Wlo, Whi)
+    assert d == (5 - 3) + (7 - 4) + (2 - 6) + (9 - 9) == 1
+    assert lo == (4 - 3) + (7 - 5) + (2 - 6) + (8 - 10) == -3
+    assert hi == (6 - 3) + (9 - 2) + (3 - 5) + (9 - 9) == 8
+    # no near-tie anywhere: the range collapses to delta
+    assert O.delta_range(W, W, W) == (1, 1, 1)
+    # one long working set uncertain by one: the range widens by one on each side
+    lo1, hi1 = W.copy(), W.copy()
+    lo1[1, 0, 1] -= 1
+    hi1[1, 0, 1] += 1
+    assert O.delta_range(W, lo1, hi1) == (1, 0, 2)
+
+
+def test_delta_range_brackets_every_alternative():
+    """Every choice of sizes inside [W_lo, W_hi] gives a delta inside the range, and both
+    ends are reached (brute force over a small random case)."""
+    rng = np.random.default_rng(12)
+    W = rng.integers(3, 9, size=(1, 3, 2))
+    Wlo = W - rng.integers(0, 2, size=W.shape)
+    Whi = W + rng.integers(0, 2, size=W.shape)
+    d, lo, hi = O.delta_range(W, Wlo, Whi)
+    seen = set()
+    for choice in itertools.product(*[range(int(a), int(b) + 1) for a, b in zip(Wlo.ravel(), Whi.ravel())]):
+        c = np.array(choice).reshape(W.shape)
+        seen.add(int((c[..., 0] - c[..., 1]).sum()))
+    assert min(seen) == lo and max(seen) == hi and lo <= d <= hi
+
+
+def test_importance_orders_deep_tail_by_value():
+    """Slots 110-130 nats below the row maximum keep their order: their probabilities
+    (about 1e-48 to 1e-57) are far above float64's range end, so keep-sets rank them by
+    value, not by age.  One row: ordering by probability is ordering by logit, so the
+    evicted slots are exactly the E lowest logits (closed form)."""
+    rng = np.random.default_rng(13)
+    n, E = 200, 16
+    lg = rng.uniform(0.0, 2.0, n)
+    deep = rng.choice(n - 8, 40, replace=False)
+    lg[deep] = -110.0 - 20.0 * rng.permutation(40) / 40.0   # distinct, 0.5 nat apart
+    _, _, a = O.softmax_stats(lg[None])
+    imp = O.importance(a)
+    assert np.all(imp[deep] > 0) and np.unique(imp[deep]).size == 40
+    kept, ev, near = O.keep_set(imp, n - E, 8)
+    assert not near
+    assert np.array_equal(ev, np.sort(np.argsort(lg)[:E]))
+    # the probabilities themselves: exp(l - M) / Z within float64 rounding
+    M = lg.max()
+    Z = math.fsum(math.exp(v - M) for v in lg)
+    for i in deep[:5]:
+        assert abs(imp[i] / (math.exp(lg[i] - M) / Z) - 1.0) < 1e-12
 
 
 # ----------------------------------------------------------------------------- keep-set (R5, R6)

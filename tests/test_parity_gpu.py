@@ -7,7 +7,7 @@ import torch
 
 import oracle as O
 from synth import workloads as SW
-from tests.parity_util import compare_step, run_step_gpu
+from tests.parity_util import compare_logits, compare_step, run_step_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -114,10 +114,12 @@ def test_config1_boundary():
     _say("[step] config1")
     s, l_ = O.ema_run(wl.queries, wl.q_dtype, wl.params["beta_s"], wl.params["beta_l"])
     res = O.boundary_step(wl, s, l_, wl.params)
-    st, out, _ = run_step_gpu(wl, sum_s=s, sum_l=l_)
+    st, out, eng = run_step_gpu(wl, sum_s=s, sum_l=l_)
     rep = compare_step(wl, np.arange(wl.B), st, out, res, wl.params["n_local"])
     assert res.decision[0] == O.DECISION_COMPACT
-    _say("config1", rep)
+    wl.sum_s, wl.sum_l = s, l_
+    errs = compare_logits(eng, wl, range(wl.B))
+    _say("config1", rep, "logit/probability errors", errs)
 
 
 def test_config2_boundary():
@@ -126,9 +128,11 @@ def test_config2_boundary():
     s, l_ = O.ema_run(wl.queries, wl.q_dtype, wl.params["beta_s"], wl.params["beta_l"])
     res = O.boundary_step(wl, s, l_, wl.params)
     assert 0 < res.counters["grows"] < wl.B
-    st, out, _ = run_step_gpu(wl, sum_s=s, sum_l=l_)
+    st, out, eng = run_step_gpu(wl, sum_s=s, sum_l=l_)
     rep = compare_step(wl, np.arange(wl.B), st, out, res, wl.params["n_local"])
-    _say("config2", rep, res.counters)
+    wl.sum_s, wl.sum_l = s, l_
+    errs = compare_logits(eng, wl, range(wl.B))
+    _say("config2", rep, res.counters, "logit/probability errors", errs)
 
 
 CASES = [
@@ -183,9 +187,10 @@ def test_direct_cases(name, kw):
     res = O.boundary_step(wl, wl.sum_s, wl.sum_l, wl.params)
     # scattered request slots inside a larger table
     slots = np.arange(wl.B) * 3 + 1
-    st, out, _ = run_step_gpu(wl, slots=slots, max_req=int(slots.max()) + 2)
+    st, out, eng = run_step_gpu(wl, slots=slots, max_req=int(slots.max()) + 2)
     rep = compare_step(wl, slots, st, out, res, wl.params["n_local"])
-    _say(name, rep, res.counters)
+    errs = compare_logits(eng, wl, range(wl.B))
+    _say(name, rep, res.counters, "logit/probability errors", errs)
 
 
 def test_rope_positions_clamped_to_the_table():
@@ -287,14 +292,38 @@ PLANTED = [
 ]
 
 
-@pytest.mark.parametrize("name,fns,params", PLANTED, ids=[c[0] for c in PLANTED])
-def test_planted_logits(name, fns, params):
-    wl = SW.planted_logits_case(zlib.crc32(name.encode()) % 10000, fns, params=params, name=name)
+def _deep_tail(rng, n, top=-110.0, step=0.5):
+    """Logits in [0, 2] except 40 slots 110-130 nats below (0.5 nat apart, never the last
+    8): their probabilities lie below float32's range, yet the keep-set must rank them by
+    value (the 16 lowest go), not by age."""
+    lg = rng.uniform(0.0, 2.0, n)
+    deep = rng.choice(n - 8, 40, replace=False)
+    lg[deep] = top - step * rng.permutation(40)
+    return lg
+
+
+# planted cases on bf16 keys (the matrix-core scan); logits x sqrt(64) exact in bf16 where it matters
+PLANTED_BF16 = [
+    # 100-119.5 nats below the maximum (exact bf16 multiples of 4 after scaling by 8)
+    ("deep_tail_bf16", [(40, lambda rng, n: _deep_tail(rng, n, top=-100.0)),
+                        (64, lambda rng, n: _deep_tail(rng, n, top=-100.0))], dict(SW.PARAMS_DEFAULT, n_local=8)),
+]
+PLANTED += [
+    ("deep_tail", [(40, _deep_tail), (90, lambda rng, n: _deep_tail(rng, n, top=-115.0, step=0.375))],
+     dict(SW.PARAMS_DEFAULT, n_local=8)),
+]
+
+
+@pytest.mark.parametrize("name,fns,params,dtype", [c + ("f32",) for c in PLANTED] + [c + ("bf16",) for c in PLANTED_BF16],
+                         ids=[c[0] for c in PLANTED] + [c[0] for c in PLANTED_BF16])
+def test_planted_logits(name, fns, params, dtype):
+    wl = SW.planted_logits_case(zlib.crc32(name.encode()) % 10000, fns, params=params, name=name, dtype=dtype)
     _say(f"[planted] {name} n={[wl.n(b) for b in range(wl.B)]}")
     res = O.boundary_step(wl, wl.sum_s, wl.sum_l, wl.params)
-    st, out, _ = run_step_gpu(wl)
+    st, out, eng = run_step_gpu(wl)
     rep = compare_step(wl, np.arange(wl.B), st, out, res, wl.params["n_local"])
-    _say(name, rep, res.counters, "W", res.W[:, 0, 0].tolist())
+    errs = compare_logits(eng, wl, range(wl.B))
+    _say(name, rep, res.counters, "W", res.W[:, 0, 0].tolist(), "logit/probability errors", errs)
 
 
 @pytest.mark.parametrize("policy", ["growpage", "random", "inverse", "always_compact", "shrink"])
