@@ -26,7 +26,8 @@ EXPORTED = ("gp_abi_version", "gp_status_string", "gp_last_hip_error_string", "g
             "gp_scratch_bytes",
             "gp_boundary_scan", "gp_decide", "gp_decide_policy", "gp_compact", "gp_compact_prepare",
             "gp_compact_move", "gp_append_kv", "gp_decode_attention", "gp_contiguous_malloc",
-            "gp_contiguous_free", "gp_scan_logits")
+            "gp_contiguous_free", "gp_scan_logits", "gp_boundary_step_static")
+GP_STATIC_SCRATCH_BYTES = 64 << 20
 # decision policies (gp_decide_policy)
 POLICIES = {"growpage": 0, "random": 1, "inverse": 2, "always_compact": 3, "shrink": 4}
 
@@ -84,6 +85,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gp_boundary_scan.restype = i32
     lib.gp_boundary_scan.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Pages), P, i32, P, P, P, P,
                                      i32, P, ctypes.POINTER(Params), P, P, P, sz, i64, P]
+    lib.gp_boundary_step_static.restype = i32
+    lib.gp_boundary_step_static.argtypes = [ctypes.POINTER(KV), ctypes.POINTER(Pages), P, i32, P, P, P, P, i32,
+                                            P, ctypes.POINTER(Params), i64, P, P, P, P, P, P, P, P]
     lib.gp_scan_logits.restype = i32
     lib.gp_scan_logits.argtypes = [ctypes.POINTER(KV), i32, i64, P, sz, i32, i32, P, P]
     lib.gp_decide.restype = i32
@@ -184,6 +188,18 @@ def boundary_scan(kv: KV, pages: Pages, req_ids, n_req, sum_s, sum_l, rope_cos, 
                                  _ptr(stats_out), _ptr(scratch), int(scratch_nbytes),
                                  int(max_total_tokens), _stream(stream))
     _check(st, "gp_boundary_scan")
+
+
+def boundary_step_static(kv: KV, pages: Pages, req_ids, n_req, sum_s, sum_l, rope_cos, rope_sin, rope_max_pos,
+                         pos, prm: Params, max_total_tokens, ws_out, stats_out, decision_out, delta_out,
+                         status_out, evicted_out=None, counters_out=None, stream=None):
+    st = load().gp_boundary_step_static(ctypes.byref(kv), ctypes.byref(pages), _ptr(req_ids), int(n_req),
+                                        _ptr(sum_s), _ptr(sum_l), _ptr(rope_cos), _ptr(rope_sin),
+                                        int(rope_max_pos), _ptr(pos), ctypes.byref(prm), int(max_total_tokens),
+                                        _ptr(ws_out), _ptr(stats_out), _ptr(decision_out), _ptr(delta_out),
+                                        _ptr(status_out), _ptr(evicted_out), _ptr(counters_out),
+                                        _stream(stream))
+    _check(st, "gp_boundary_step_static")
 
 
 def scan_logits(kv: KV, n_req, max_total_tokens, scratch, scratch_nbytes, entry, n, logits_out, stream=None):

@@ -12,6 +12,12 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 thread_local hipError_t g_last_hip_error = hipSuccess;
 
+}  // namespace
+
+void gp::note_hip_error(hipError_t e) { g_last_hip_error = e; }
+
+namespace {
+
 gp_status from_hip(hipError_t e) {
   if (e == hipSuccess) return GP_OK;
   g_last_hip_error = e;

@@ -129,6 +129,9 @@ struct Geo {
   int32_t n_req;
 };
 
+// The HIP error gp_last_hip_error_string() reports (kept per host thread).
+void note_hip_error(hipError_t e);
+
 // ----------------------------------------------------------------------------- launchers
 hipError_t launch_ema(const void* q, int32_t q_dtype, int64_t sr, int64_t sl, int64_t sh,
                       const int32_t* req_ids, int32_t n_req, int32_t L, int32_t Hq, int32_t d,

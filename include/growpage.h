@@ -275,6 +275,32 @@ gp_status gp_compact_move(const gp_kv* kv, const gp_pages* pages, const int32_t*
                           int32_t n_req, int32_t* counters_out, void* scratch,
                           size_t scratch_bytes, int64_t max_total_tokens, void* stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation: one boundary batch, exactly
+ * gp_boundary_scan, then gp_decide_policy (GP_POLICY_SHRINK when params->shrink is 1,
+ * else GP_POLICY_GROWPAGE), then gp_compact, with the same arguments, outputs and errors,
+ * but no caller scratch: the scratch is a buffer of GP_STATIC_SCRATCH_BYTES that the
+ * library holds on each device until the process ends.  Nothing is allocated: the
+ * buffer's device address is looked up once per device (on the first call with that
+ * device current) and kept.  Runs on the current device; `stream` must belong to it.
+ * A batch whose gp_scratch_bytes(kv, n_req, max_total_tokens) exceeds
+ * GP_STATIC_SCRATCH_BYTES returns GP_ERR_SCRATCH before anything is launched (64 MiB:
+ * for example 16 requests of up to 8192 tokens on one layer of the 8B shape, or about
+ * 7,000 tokens across all 32 layers).  The buffer keeps the last call's contents; every
+ * region a call reads is written by that call first, so nothing needs clearing.  Calls
+ * on one device share the buffer: two calls that can run at the same time on one device
+ * (different streams or host threads without ordering) race and corrupt each other's
+ * results; order them (one stream, or events).  evicted_out and counters_out may be NULL
+ * as in gp_compact; decision_out, delta_out and status_out are required. */
+#define GP_STATIC_SCRATCH_BYTES (64 << 20)
+gp_status gp_boundary_step_static(const gp_kv* kv, const gp_pages* pages, const int32_t* req_ids,
+                                  int32_t n_req, const float* sum_s, const float* sum_l,
+                                  const float* rope_cos, const float* rope_sin, int32_t rope_max_pos,
+                                  const int32_t* pos, const gp_params* params, int64_t max_total_tokens,
+                                  int32_t* ws_out, float* stats_out, uint8_t* decision_out,
+                                  int32_t* delta_out, int32_t* status_out, int32_t* evicted_out,
+                                  int32_t* counters_out, void* stream);
+
 /* Deployment helper (not part of the boundary path): physically contiguous device memory
  * for the K/V pools, with the signatures of a PyTorch pluggable allocator
  * (torch.cuda.memory.CUDAPluggableAllocator).  The compaction's row moves address pool
