@@ -78,8 +78,8 @@ def parse():
                          "of 1-20 GiB between them): per-placement step and gather times on their "
                          "own line, to show how the physical pages set the gather's speed")
     ap.add_argument("--paper", action="store_true",
-                    help="boundary sweep at the pages' operating point (KV block 256, p 0.99, quota 64), "
-                         "reported on its own line")
+                    help="the boundary sweep (or, with --workload decode_loop, the decode loop) at the pages' "
+                         "operating point (KV block 256, p 0.99, quota 64), reported on its own line")
     return ap.parse_args()
 
 
@@ -377,7 +377,7 @@ def placements(args):
 def decode_loop(args):
     """The decode loop on the Qwen3-8B shape: 128 requests from 1024-token prompts, 36
     layers, every step updates both summaries and appends one K/V row per request, every
-    16th step all 128 requests run a boundary batch.  Input generation is outside the
+    P-th step (16; 256 with --paper) all 128 requests run a boundary batch.  Input generation is outside the
     timed region; every library call of every step is inside it (HIP events per step).
     With --graphs each step replays a HIP graph of its library calls (one launch); on
     MI355X that measured the same as eager launches (0.611 against 0.607 ms per step):
@@ -390,7 +390,11 @@ def decode_loop(args):
     from synth.decode_loop import DecodeLoopGen, DecodeSpec
 
     Bd.load()
-    spec = DecodeSpec(steps=args.decode_steps)
+    if args.paper:   # the pages' operating point: KV block 256, p 0.99, quota 64
+        from synth import workloads as SW
+        spec = DecodeSpec(steps=args.decode_steps, P=256, params=dict(SW.PARAMS_PAPER))
+    else:
+        spec = DecodeSpec(steps=args.decode_steps)
     gen = DecodeLoopGen(spec, "cuda", contiguous=not args.ordinary_pools)
     st = gen.initial_state()
     torch.cuda.synchronize()
@@ -466,8 +470,10 @@ def decode_loop(args):
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"decode_loop: 128 requests x 36 layers, 32q/8kv heads, d128, bf16 K/V, page 16, "
-                               f"1024-token prompts, {spec.steps} decode steps, boundary every 16 steps",
+        "config": {"workload": f"decode_loop{'_paper' if args.paper else ''}: 128 requests x 36 layers, 32q/8kv "
+                               f"heads, d128, bf16 K/V, page {spec.P}, "
+                               + ("p 0.99, quota 64, " if args.paper else "")
+                               + f"1024-token prompts, {spec.steps} decode steps, boundary every {spec.P} steps",
                    "requests": spec.B, "layers": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "page_size": spec.P, "prompt": spec.prompt, "pool_pages": spec.num_pages,
                    "top_p": spec.params["top_p"], "n_local": spec.params["n_local"], "seed": spec.seed,
