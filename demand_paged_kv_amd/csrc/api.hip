@@ -46,7 +46,9 @@ gp_status check_kv(const gp_kv* kv) {
   if ((kv->stride_layer * esz) % 16 || (kv->stride_page * esz) % 16 || (kv->stride_head * esz) % 16 ||
       (kv->stride_tok * esz) % 16)
     return GP_ERR_INVALID;
-  if (kv->Hq != kGroup * kv->Hkv) return GP_ERR_UNSUPPORTED;
+  if (kv->Hq % kv->Hkv != 0) return GP_ERR_UNSUPPORTED;
+  const int32_t G = kv->Hq / kv->Hkv;
+  if (G != 1 && G != 2 && G != kGroup) return GP_ERR_UNSUPPORTED;
   if (kv->d != 64 && kv->d != 128) return GP_ERR_UNSUPPORTED;
   if (kv->P % 8 != 0 || kv->P > 256) return GP_ERR_UNSUPPORTED;
   return GP_OK;
@@ -70,6 +72,7 @@ Geo make_geo(const gp_kv* kv, const gp_pages* pg, const int32_t* req_ids, int32_
   g.L = kv->L;
   g.Hq = kv->Hq;
   g.Hkv = kv->Hkv;
+  g.G = kv->Hq / kv->Hkv;
   g.d = kv->d;
   g.P = kv->P;
   g.num_pages = kv->num_pages;

@@ -70,7 +70,8 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a) {
   const int c0 = (j * EL) & (D / 2 - 1);
 #pragma unroll
   for (int h = 0; h < kGroup; ++h) {
-    const int64_t qo = (int64_t)b * a.q_sr + (int64_t)l * a.q_sl + (int64_t)(kvh * kGroup + h) * a.q_sh;
+    // slots beyond the group (G < 4) repeat its last head; only real heads are written
+    const int64_t qo = (int64_t)b * a.q_sr + (int64_t)l * a.q_sl + (int64_t)(kvh * g.G + min(h, g.G - 1)) * a.q_sh;
 #pragma unroll
     for (int e = 0; e < EL; ++e) {
       float x1, x2;
@@ -161,7 +162,8 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a) {
   if (tl == 0) {
 #pragma unroll
     for (int h = 0; h < kGroup; ++h) {
-      float* o = a.out + ((((int64_t)b * g.L + l) * g.Hq) + kvh * kGroup + h) * D + j * EL;
+      if (h >= g.G) break;
+      float* o = a.out + ((((int64_t)b * g.L + l) * g.Hq) + kvh * g.G + h) * D + j * EL;
 #pragma unroll
       for (int e = 0; e < EL; ++e) o[e] = acc[h][e];
     }

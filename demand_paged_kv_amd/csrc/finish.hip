@@ -383,9 +383,11 @@ __device__ __forceinline__ void finish_unit(const FinishArgs& a, int rank, int l
   const int wave = tid >> 6;
   const int b = a.sp.order[rank];
   const int64_t u = ((int64_t)b * g.L + l) * g.Hkv + kvh;
-  auto widx = [&](int k) { return (((int64_t)b * g.L + l) * g.Hq + kvh * kGroup + (k >> 1)) * 2 + (k & 1); };
+  // statistics / working-set index of row k (rows of a missing head read their twin's)
+  auto widx = [&](int k) { return (((int64_t)b * g.L + l) * g.Hq + kvh * g.G + row_head(k, g.G)) * 2 + (k & 1); };
+  const bool real_row = tid < kDists && row_real(tid, g.G);
   if (a.sp.flags[b]) {
-    if (tid < kDists) a.ws_out[widx(tid)] = -1;
+    if (real_row) a.ws_out[widx(tid)] = -1;
     return;
   }
   const int n = a.sp.n_tok[b];
@@ -399,7 +401,7 @@ __device__ __forceinline__ void finish_unit(const FinishArgs& a, int rank, int l
   const float* x = a.sp.logits + ubase;
 
   if (n == 0) {
-    if (tid < kDists) {
+    if (real_row) {
       a.ws_out[widx(tid)] = 0;
       a.sp.stats[widx(tid) * 2 + 1] = 0.f;
       if (a.stats_out) {
@@ -658,7 +660,7 @@ __device__ __forceinline__ void finish_unit(const FinishArgs& a, int rank, int l
     }
     __syncthreads();
   }
-  if (tid < kDists) {
+  if (real_row) {
     const int k = tid;
     a.ws_out[widx(k)] = s_W[k];
     const float Zf = (float)((double)s_Z[k] / (double)kMassScale);
@@ -729,9 +731,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void f
       for (int i = 0; i < 4; ++i) s_mw[wave][4 * (lane >> 4) + i] = mx[i];
     }
     __syncthreads();
-    if (tid < kDists) {
+    if (tid < kDists && row_real(tid, g.G)) {
       const float m = fmaxf(fmaxf(s_mw[0][tid], s_mw[1][tid]), fmaxf(s_mw[2][tid], s_mw[3][tid]));
-      const int h = kvh * kGroup + (tid >> 1);
+      const int h = kvh * g.G + (tid >> 1);
       s.sp.stats[((((int64_t)b * g.L + l) * g.Hq + h) * 2 + (tid & 1)) * 2] = m;
     }
     __syncthreads();  // the unit's logits and maxima are visible to the whole block

@@ -9,8 +9,8 @@
 
 namespace gp {
 
-constexpr int kDists = 8;          // 4 query heads per KV head x 2 summaries
-constexpr int kGroup = 4;          // query heads per KV head
+constexpr int kDists = 8;          // score rows per unit: 4 query-head slots x 2 summaries
+constexpr int kGroup = 4;          // query-head slots per unit (the largest group supported)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int64_t kMaxSlots = 1 << 24;  // candidate slots per request (max_pages * P) the scan indexes
 constexpr int kReqFields = 8;      // per-request int32 fields of the compaction plan
@@ -19,6 +19,13 @@ constexpr int kLogitAlign = 16;    // each unit's logit rows start on a 512-byte
 // Token rows a unit of n candidate slots takes in the logit scratch: n rounded up to a
 // multiple of kLogitAlign, so that every 16-token store covers whole cache lines.
 __host__ __device__ inline int64_t logit_rows(int64_t n) { return (n + kLogitAlign - 1) / kLogitAlign * kLogitAlign; }
+
+// Query head (within its KV head's group of G = Hq / Hkv in {1, 2, 4}) that score row k of a
+// unit scores: rows 2j, 2j+1 belong to head j; with G < 4 the rows of the missing heads
+// repeat the last head's (equal logits: no change to any working set or to the max-of-rows
+// importance), and only rows of real heads (row_real) are written out.
+__host__ __device__ inline int row_head(int k, int G) { return min(k >> 1, G - 1); }
+__host__ __device__ inline bool row_real(int k, int G) { return (k >> 1) < G; }
 
 // Evicted slots per unit: at the boundary n = (A+1)P, so a compaction evicts P slots,
 // or 2P when it shrinks the allocation by a page.
@@ -120,6 +127,7 @@ struct Geo {
   const void* v;
   int64_t s_layer, s_page, s_head, s_tok;
   int32_t L, Hq, Hkv, d, P, num_pages;
+  int32_t G;          // query heads per KV head: 1, 2 or 4
   int32_t dtype;
   const int32_t* page_table;
   int32_t max_pages;

@@ -50,7 +50,7 @@ struct MfmaSummaries {
     const bool rope = a.rope_cos != nullptr;
     const int pos = rope ? min(max(a.pos[r], 0), a.rope_max_pos - 1) : 0;
     const float* s = ((col & 1) ? a.sum_l : a.sum_s) +
-                     (((int64_t)r * g.L + l) * g.Hq + kvh * kGroup + ((col & 7) >> 1)) * D;
+                     (((int64_t)r * g.L + l) * g.Hq + kvh * g.G + row_head(col & 7, g.G)) * D;
 #pragma unroll
     for (int k = 0; k < KS / 2; ++k) {
 #pragma unroll

@@ -163,7 +163,7 @@ __global__ __launch_bounds__(64) void logit_kernel(ScanArgs a) {
   for (int i = 0; i < 8; ++i) {
     const int dist = slot_dist(js, i);
     const float* s = ((dist & 1) ? a.sum_l : a.sum_s) +
-                     (((int64_t)r * g.L + l) * g.Hq + kvh * kGroup + (dist >> 1)) * D;
+                     (((int64_t)r * g.L + l) * g.Hq + kvh * g.G + row_head(dist, g.G)) * D;
 #pragma unroll
     for (int e = 0; e < EL; ++e) {
       const float x1 = s[c0 + e];
@@ -258,8 +258,8 @@ __global__ __launch_bounds__(64) void logit_kernel(ScanArgs a) {
   }
   m = fmaxf(m, __shfl_xor(m, 16, 64));
   m = fmaxf(m, __shfl_xor(m, 32, 64));
-  if (lane < 8) {
-    const int h = kvh * kGroup + (js >> 1);
+  if (lane < 8 && row_real(js, g.G)) {
+    const int h = kvh * g.G + (js >> 1);
     const int64_t si = ((((int64_t)b * g.L + l) * g.Hq + h) * 2 + (js & 1)) * 2;
     a.sp.stats[si] = m;
   }

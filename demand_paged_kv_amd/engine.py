@@ -144,7 +144,8 @@ class BoundaryEngine:
 
     def scan_logits(self, entry: int, n: int, stream=None) -> torch.Tensor:
         """The last scan's logits of batch entry ``entry`` (n candidate slots) as a new
-        [L][Hkv][n][8] float32 tensor, row 2*j + s = query head 4g + j, summary s."""
+        [L][Hkv][n][8] float32 tensor, row 2*j + s = query head G*g + min(j, G-1) of KV head g
+        (G = Hq / Hkv), summary s."""
         st = self.st
         out = torch.empty((st.L, st.Hkv, int(n), 8), dtype=torch.float32, device=st.k_pool.device)
         B.scan_logits(self.kv, self._scan_batch, self.max_total_tokens, self.scratch, self.scratch_nbytes,

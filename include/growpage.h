@@ -115,7 +115,7 @@ typedef struct gp_params {
 /* Paged K/V pools (host struct).  Element (layer l, page p, KV head g, slot s, i) of
  * K lives at k + l*stride_layer + p*stride_page + g*stride_head + s*stride_tok + i
  * (strides in elements, the d elements of a row contiguous); V likewise.  Rows must
- * be 16-byte aligned.  Supported: Hq == 4*Hkv, d in {64, 128}, P a multiple of 8. */
+ * be 16-byte aligned.  Supported: Hq == G*Hkv with G in {1, 2, 4}, d in {64, 128}, P a multiple of 8. */
 typedef struct gp_kv {
   int32_t L, Hq, Hkv, d, P, num_pages;
   int32_t dtype;                 /* gp_dtype of K and V */
@@ -178,7 +178,7 @@ size_t gp_scratch_bytes(const gp_kv* kv, int32_t n_req, int64_t max_total_tokens
  * statistics are also kept in `scratch` for gp_compact, so the same scratch must be
  * passed to gp_compact unchanged.  The page state is only read.
  * Errors: GP_ERR_INVALID (NULL/shape), GP_ERR_SCRATCH (scratch too small),
- * GP_ERR_UNSUPPORTED (Hq != 4*Hkv, d not 64/128, P % 8 != 0, max_pages * P > 2^24). */
+ * GP_ERR_UNSUPPORTED (Hq / Hkv not 1, 2 or 4, d not 64/128, P % 8 != 0, max_pages * P > 2^24). */
 gp_status gp_boundary_scan(const gp_kv* kv, const gp_pages* pages, const int32_t* req_ids,
                            int32_t n_req, const float* sum_s, const float* sum_l,
                            const float* rope_cos, const float* rope_sin, int32_t rope_max_pos,
@@ -190,7 +190,8 @@ gp_status gp_boundary_scan(const gp_kv* kv, const gp_pages* pages, const int32_t
  * each summary is scored against every retained key), for inspection and parity checks:
  * copies batch entry `entry`'s scores from `scratch` (the scan's, unchanged since; n_req
  * and max_total_tokens as passed to it) to logits_out [L][Hkv][n][8] float32, row
- * 2*j + s being query head g*4 + j of KV head g under summary s (0 short, 1 long),
+ * 2*j + s being query head g*G + min(j, G-1) of KV head g (G = Hq/Hkv: with G < 4 the
+ * rows of j >= G repeat head G-1) under summary s (0 short, 1 long),
  * scaled by 1/sqrt(d) and rotated as the scan did.  n: the entry's candidate slots
  * n_alloc*P + fill; slots the scan did not score (t >= its count, or an entry flagged
  * GP_REQ_OVERFLOW) read NaN.  gp_compact leaves the scores in place.

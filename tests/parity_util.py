@@ -440,6 +440,9 @@ def compare_logits(eng, wl, entries, host_idx=None):
         cr = sr = None
         if wl.rope_cos is not None:
             cr, sr = wl.rope_cos[wl.pos[i]], wl.rope_sin[wl.pos[i]]
+        # with fewer than 4 query heads per KV head, rows of the missing heads repeat the last
+        for j in range(G, 4):
+            assert np.array_equal(lg_gpu[..., 2 * j:2 * j + 2], lg_gpu[..., 2 * G - 2:2 * G]), ("row copy", b, j)
         for l in range(wl.L):
             for g in range(wl.Hkv):
                 kf = O.widen(wl.k_rows[i][l, g], wl.dtype)

@@ -68,7 +68,12 @@ def test_invalid_arguments_rejected_on_host(lib):
     args = lambda k=kv, p=pg, pr=prm, n=1, scr=0x10000, nb=1 << 40: (
         P(k), P(p), 0x9000, n, 0xa000, 0xb000, None, None, 0, None, P(pr), 0xc000, None, scr, nb, 10, None)
     assert lib.gp_boundary_scan(*args(k=_kv(k=None))) == B.GP_ERR_INVALID
-    assert lib.gp_boundary_scan(*args(k=_kv(Hq=24))) == B.GP_ERR_UNSUPPORTED
+    assert lib.gp_boundary_scan(*args(k=_kv(Hq=24))) == B.GP_ERR_UNSUPPORTED      # group of 3
+    assert lib.gp_boundary_scan(*args(k=_kv(Hq=64))) == B.GP_ERR_UNSUPPORTED      # group of 8
+    assert lib.gp_boundary_scan(*args(k=_kv(Hq=12))) == B.GP_ERR_UNSUPPORTED      # not a multiple
+    assert lib.gp_boundary_scan(*args(k=_kv(Hq=4))) == B.GP_ERR_UNSUPPORTED       # fewer than Hkv
+    for hq in (8, 16):                                                             # groups of 1 and 2 pass
+        assert lib.gp_boundary_scan(*args(k=_kv(Hq=hq), n=-1)) == B.GP_ERR_INVALID
     assert lib.gp_boundary_scan(*args(k=_kv(d=96))) == B.GP_ERR_UNSUPPORTED
     assert lib.gp_boundary_scan(*args(k=_kv(P=12))) == B.GP_ERR_UNSUPPORTED
     assert lib.gp_boundary_scan(*args(k=_kv(stride_tok=64))) == B.GP_ERR_INVALID

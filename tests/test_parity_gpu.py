@@ -175,6 +175,14 @@ CASES = [
     # the last one is empty (n = 0)
     ("zero_alloc", dict(B=6, L=2, Hq=8, Hkv=2, d=64, P=16, alloc=[0, 0, 0, 1, 3, 0], fill=[16, 16, 16, 16, 16, 0],
                         grow_frac=0.6, params=dict(SW.PARAMS_DEFAULT, n_local=8))),
+    # GQA groups below 4 query heads per KV head (multi-head G = 1, G = 2), on the matrix-core
+    # scan (bf16, P % 16 == 0) and the vector-unit scan (float32 or P = 24)
+    ("gqa1_bf16_d128_p16", dict(B=5, L=2, Hq=8, Hkv=8, d=128, P=16, ctx=(100, 900), grow_frac=0.5)),
+    ("gqa2_bf16_d64_p16", dict(B=5, L=2, Hq=4, Hkv=2, d=64, P=16, ctx=(60, 700), grow_frac=0.5)),
+    ("gqa2_f32_d128_p8", dict(B=4, L=1, Hq=8, Hkv=4, d=128, P=8, dtype="f32", ctx=(9, 400))),
+    ("gqa1_bf16_d64_p24", dict(B=4, L=2, Hq=4, Hkv=4, d=64, P=24, ctx=(30, 800))),
+    ("gqa1_p256_cow", dict(B=5, L=1, Hq=2, Hkv=2, d=128, P=256, grow_frac=0.2, prefix_groups=2, prefix_pages=2,
+                           ctx=(300, 1500), spare_pages=12, params=dict(SW.PARAMS_PAPER))),
     # 128K-token units: a unit's logits (4 MB) far beyond the selection's LDS buffers
     ("long_unit_128k", dict(B=2, L=1, Hq=32, Hkv=8, d=128, P=16, ctx=(131072, 131072), grow_frac=0.5)),
 ]

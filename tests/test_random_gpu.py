@@ -1,7 +1,7 @@
 """Seeded random boundary batches against the oracle.
 
 Each case draws, from its own seed, a batch shape (1-8 requests, 1-3 layers, 1/2/8 KV heads
-with 4 query heads each, head_dim 64 or 128), storage (bf16 or float32), page size (8 to
+with 1, 2 or 4 query heads each, head_dim 64 or 128), storage (bf16 or float32), page size (8 to
 256 tokens, including sizes that are not multiples of 16, which take the vector-unit
 scan), contexts, prefix sharing, pool pressure (free pages, full page-table rows),
 requests off their boundary, RoPE or none, Top-p, tau, the local quota and a decision
@@ -26,6 +26,8 @@ SEEDS = list(range(7100, 7260))
 
 def _draw(seed):
     rng = np.random.default_rng(seed)
+    # the group size from a stream of its own, so the other draws do not depend on it
+    G = int(np.random.default_rng([seed, 1]).choice([1, 2, 4, 4]))
     Hkv = int(rng.choice([1, 2, 8]))
     d = int(rng.choice([64, 128]))
     P = int(rng.choice([8, 16, 16, 24, 32, 48, 64, 128, 256]))
@@ -42,7 +44,7 @@ def _draw(seed):
     policy = str(rng.choice(["growpage"] * 5 + ["shrink", "inverse", "random", "always_compact"]))
     params = dict(beta_s=0.9, beta_l=0.999, top_p=float(rng.choice([0.5, 0.9, 0.95, 0.99, 0.999])),
                   tau=int(rng.choice([0, 0, 0, 50, -50])), n_local=int(rng.choice([0, 4, 16, 64])))
-    kw = dict(B=B, L=L, Hq=4 * Hkv, Hkv=Hkv, d=d, P=P, dtype=dtype, ctx=(lo, hi),
+    kw = dict(B=B, L=L, Hq=G * Hkv, Hkv=Hkv, d=d, P=P, dtype=dtype, ctx=(lo, hi),
               spare_pages=int(rng.integers(0, 40)), grow_frac=float(rng.uniform(0, 1)),
               rope=bool(rng.random() < 0.85), prefix_groups=prefix_groups, prefix_pages=prefix_pages,
               fill=fill, params=params)
@@ -60,7 +62,7 @@ def test_random_batch(seed):
     from demand_paged_kv_amd.engine import BoundaryEngine
     wl, policy, u, grow_prob = _draw(seed)
     prm = dict(wl.params, policy=policy, rand_u=u, grow_prob=grow_prob)
-    print(f"[random] seed {seed}: B={wl.B} L={wl.L} Hkv={wl.Hkv} d={wl.d} P={wl.P} {wl.dtype} "
+    print(f"[random] seed {seed}: B={wl.B} L={wl.L} Hq={wl.Hq} Hkv={wl.Hkv} d={wl.d} P={wl.P} {wl.dtype} "
           f"tokens={wl.total_tokens()} policy={policy} params={wl.params}", flush=True)
     res = O.boundary_step(wl, wl.sum_s, wl.sum_l, prm)
     if res.ambiguous.any():
