@@ -3,7 +3,8 @@
 // from Zipage?": the engine sits inside PagedAttention serving, next to the decode
 // kernel that reads the compacted pages).
 //
-// One wave per (entry, layer, KV head) unit serves the unit's 4 query heads.  Like the
+// One wave per (entry, layer, KV head) unit serves the unit's G <= 4 query heads (4 slots;
+// with G < 4 the spare slots repeat the last head and are not written).  Like the
 // scan, 16 lanes share a token row (lane j holds D/16 contiguous elements of K and V)
 // and a wave step covers 4 tokens of one page.  Each lane keeps the slices of the 4
 // rotated queries (pre-scaled by log2(e)/sqrt(d)), a 16-lane butterfly of DPP rotations

@@ -11,7 +11,7 @@
 //   logit_kernel   one wave per unit, launched longest-first.  The wave streams the
 //                  unit's K rows through the page table once; 16 lanes share a token row
 //                  (each holds D/16 contiguous elements), every lane keeps the matching
-//                  slices of all 8 rotated summaries (4 query heads x 2 timescales) in
+//                  slices of all 8 rotated summaries (4 query-head slots x 2 timescales) in
 //                  registers, and a DPP transpose-reduce (3 steps within each 8-lane half,
 //                  one across the halves) leaves lane j with the logit of summary j mod 8
 //                  for its token.  Logits go to the scratch ([unit][n'][8] float32, n'
