@@ -21,7 +21,7 @@ from tests.parity_util import compare_logits, compare_step
 
 pytestmark = pytest.mark.gpu
 
-SEEDS = list(range(7100, 7260))
+SEEDS = list(range(7100, 7700))
 
 
 def _draw(seed):
