@@ -126,6 +126,34 @@ class BoundaryEngine:
             if t is not None and t.is_cuda:
                 t.record_stream(s)
 
+    def _ids(self, req_ids: torch.Tensor) -> int:
+        """Host-side check of a request-id tensor (the kernels index the page table with
+        its entries unchecked): int32, contiguous, on the state's device, at most the
+        engine's batch.  Returns its length."""
+        dev = self.st.k_pool.device
+        if not (isinstance(req_ids, torch.Tensor) and req_ids.dtype == torch.int32 and req_ids.dim() == 1
+                and req_ids.is_contiguous() and req_ids.device == dev):
+            raise ValueError(f"request ids must be a contiguous 1-D int32 tensor on {dev}")
+        nb = int(req_ids.numel())
+        if nb > self.max_batch:
+            raise ValueError(f"batch of {nb} requests exceeds the engine's maximum of {self.max_batch}")
+        return nb
+
+    def _rows(self, x: torch.Tensor, nb: int, heads: int, what: str):
+        """Host-side shape and device check of a per-request [n][L][heads][d] tensor."""
+        st = self.st
+        if tuple(x.shape) != (nb, st.L, heads, st.d) or x.device != st.k_pool.device or x.stride(3) != 1:
+            raise ValueError(f"{what} must be [{nb}][{st.L}][{heads}][{st.d}] with d contiguous on "
+                             f"{st.k_pool.device}, got {tuple(x.shape)}")
+
+    @staticmethod
+    def _qdtype(q: torch.Tensor) -> int:
+        if q.dtype == torch.bfloat16:
+            return B.GP_BF16
+        if q.dtype == torch.float32:
+            return B.GP_F32
+        raise ValueError(f"queries must be bfloat16 or float32, got {q.dtype}")
+
     def _view_evicted(self):
         """Evicted-slot rows are P wide, 2P under SHRINK (gp_compact's evicted_out)."""
         st, n = self.st, self.max_batch
@@ -133,7 +161,7 @@ class BoundaryEngine:
         self.out.evicted = self._ev_store[: n * st.L * st.Hkv * E].view(n, st.L, st.Hkv, E)
 
     def scan(self, req_ids: torch.Tensor, stream=None):
-        st, o, nb = self.st, self.out, int(req_ids.numel())
+        st, o, nb = self.st, self.out, self._ids(req_ids)
         max_pos = 0 if st.rope_cos is None else int(st.rope_cos.shape[0])
         B.boundary_scan(self.kv, self.pages, req_ids, nb, st.sum_s, st.sum_l, st.rope_cos,
                         st.rope_sin, max_pos, st.pos if st.rope_cos is not None else None, self.prm,
@@ -154,7 +182,7 @@ class BoundaryEngine:
         return out
 
     def decide(self, req_ids: torch.Tensor, stream=None):
-        st, o, nb = self.st, self.out, int(req_ids.numel())
+        st, o, nb = self.st, self.out, self._ids(req_ids)
         if self.policy == "growpage":
             B.decide(o.ws, req_ids, nb, st.L, st.Hq, st.P, self.prm, self.pages, o.decision, o.delta,
                      o.status, o.counters, stream)
@@ -175,27 +203,26 @@ class BoundaryEngine:
         self._view_evicted()
 
     def compact(self, req_ids: torch.Tensor, stream=None):
-        o, nb = self.out, int(req_ids.numel())
+        o, nb = self.out, self._ids(req_ids)
         B.compact(self.kv, self.pages, req_ids, o.decision, nb, self.prm, o.evicted, o.status,
                   o.counters, self.scratch, self.scratch_nbytes, self.max_total_tokens, stream)
         self._tie(stream, req_ids)
 
     def compact_prepare(self, req_ids: torch.Tensor, stream=None):
-        o, nb = self.out, int(req_ids.numel())
+        o, nb = self.out, self._ids(req_ids)
         B.compact_prepare(self.kv, self.pages, req_ids, o.decision, nb, self.prm, o.evicted, o.status,
                           self.scratch, self.scratch_nbytes, self.max_total_tokens, stream)
         self._tie(stream, req_ids)
 
     def compact_move(self, req_ids: torch.Tensor, stream=None):
-        nb = int(req_ids.numel())
+        nb = self._ids(req_ids)
         B.compact_move(self.kv, self.pages, req_ids, nb, self.out.counters, self.scratch,
                        self.scratch_nbytes, self.max_total_tokens, stream)
         self._tie(stream, req_ids)
 
     def step(self, req_ids: torch.Tensor, stream=None) -> StepOutputs:
         """One boundary batch: scan, decide (+grow), compact.  Asynchronous."""
-        assert req_ids.dtype == torch.int32 and req_ids.is_cuda
-        assert int(req_ids.numel()) <= self.max_batch
+        self._ids(req_ids)
         self.scan(req_ids, stream)
         self.decide(req_ids, stream)
         self.compact(req_ids, stream)
@@ -204,17 +231,23 @@ class BoundaryEngine:
     def update_summaries(self, q: torch.Tensor, req_ids: torch.Tensor, stream=None):
         """q: [n][L][Hq][d] float32 or bfloat16 (d contiguous)."""
         st = self.st
-        qd = B.GP_BF16 if q.dtype == torch.bfloat16 else B.GP_F32
+        nb = self._ids(req_ids)
+        self._rows(q, nb, st.Hq, "q")
+        qd = self._qdtype(q)
         B.update_summaries(q, qd, (q.stride(0), q.stride(1), q.stride(2)), req_ids,
-                           int(req_ids.numel()), st.L, st.Hq, st.d, st.sum_s, st.sum_l, self.prm,
+                           nb, st.L, st.Hq, st.d, st.sum_s, st.sum_l, self.prm,
                            stream)
         self._tie(stream, q, req_ids)
 
     def append(self, k_new: torch.Tensor, v_new: torch.Tensor, req_ids: torch.Tensor,
                status_out: Optional[torch.Tensor] = None, stream=None):
         """k_new, v_new: [n][L][Hkv][d] of the pool dtype, contiguous."""
-        assert k_new.is_contiguous() and v_new.is_contiguous()
-        B.append_kv(self.kv, self.pages, k_new, v_new, req_ids, int(req_ids.numel()), status_out,
+        nb = self._ids(req_ids)
+        for x, what in ((k_new, "k_new"), (v_new, "v_new")):
+            self._rows(x, nb, self.st.Hkv, what)
+            if not x.is_contiguous() or x.dtype != self.st.k_pool.dtype:
+                raise ValueError(f"{what} must be contiguous and of the pool's dtype {self.st.k_pool.dtype}")
+        B.append_kv(self.kv, self.pages, k_new, v_new, req_ids, nb, status_out,
                     stream)
         self._tie(stream, k_new, v_new, req_ids, status_out)
 
@@ -222,11 +255,15 @@ class BoundaryEngine:
         """out[b][l][h] = attention of q[b][l][h] (pre-RoPE, rotated to st.pos) over the
         request's retained slots; q [n][L][Hq][d] bf16/float32, out float32 contiguous."""
         st = self.st
-        qd = B.GP_BF16 if q.dtype == torch.bfloat16 else B.GP_F32
+        nb = self._ids(req_ids)
+        self._rows(q, nb, st.Hq, "q")
+        qd = self._qdtype(q)
         max_pos = 0 if st.rope_cos is None else int(st.rope_cos.shape[0])
-        assert out.dtype == torch.float32 and out.is_contiguous()
+        if out.dtype != torch.float32 or not out.is_contiguous() or out.shape[0] < nb:
+            raise ValueError("out must be a contiguous float32 [n][L][Hq][d] tensor")
+        self._rows(out[:nb], nb, st.Hq, "out")
         B.decode_attention(self.kv, self.pages, q, qd, (q.stride(0), q.stride(1), q.stride(2)), req_ids,
-                           int(req_ids.numel()), st.rope_cos, st.rope_sin, max_pos,
+                           nb, st.rope_cos, st.rope_sin, max_pos,
                            st.pos if st.rope_cos is not None else None, out, stream)
         self._tie(stream, q, req_ids, out)
 
