@@ -260,9 +260,9 @@ __device__ __forceinline__ int shift_of(const int* thr, int E, int j) {
 // are adjacent in the grid, so both pools are walked together (on physically contiguous
 // pools this measured 7.4 ms against 8.3 ms for all K blocks before all V blocks on the
 // 32-layer sweep; on scattered pools the two orders tie).  A step moves 128 destination
-// rows; in each of its load/store instructions the 256
-// threads cover 256/CPR whole rows contiguously (lane t takes 16-byte piece t % CPR of a
-// row), so every store writes complete cache lines.
+// rows per 256 threads; in each of its load/store instructions the block's THREADS
+// threads cover THREADS/CPR whole rows contiguously (lane t takes 16-byte piece t % CPR
+// of a row), so every store writes complete cache lines.
 //
 // Two forms of a step.  By default the page ids are read through a pointer that may
 // point at LDS or at the global table, so each of a step's loads waits for the one
@@ -270,11 +270,13 @@ __device__ __forceinline__ int shift_of(const int* thr, int E, int j) {
 // measured 1% faster on the 32-layer sweep.  HOIST reads the ids as LDS (or global) and
 // issues all of a step's loads together, which is what counts when the grid is too
 // small to fill the chip and each block's walk through its unit is a latency chain.
-template <int CPR, bool HOIST>  // 16-byte pieces per row; all of a step's loads in flight
-__global__ __launch_bounds__(256) void gather_kernel(CompactArgs a) {
+// A grid of at most one block per CU takes blocks of 1024 threads (THREADS), which move
+// 512 rows per step: a quarter of the steps in each block's chain.
+template <int CPR, bool HOIST, int THREADS = 256>  // 16-byte pieces per row; all of a step's loads in flight
+__global__ __launch_bounds__(THREADS) void gather_kernel(CompactArgs a) {
   const Geo& g = a.g;
-  constexpr int ROWS = 128;            // destination rows per step
-  constexpr int RPI = 256 / CPR;       // rows per instruction
+  constexpr int ROWS = 128 * THREADS / 256;  // destination rows per step
+  constexpr int RPI = THREADS / CPR;         // rows per instruction
   constexpr int NI = ROWS / RPI;       // instructions per step
   __shared__ int s_thr[2 * 256];  // E <= 2P <= 512
   __shared__ int s_pt[kPtLds];
@@ -295,9 +297,9 @@ __global__ __launch_bounds__(256) void gather_kernel(CompactArgs a) {
   if (e >= k) return;
   const int32_t* ptg = a.pg.page_table + (int64_t)r * g.max_pages;
   const bool pt_lds = A + 1 <= kPtLds;
-  for (int i = tid; i < E; i += 256) s_thr[i] = a.sp.ev[u * ev_stride(P) + i] - i;
+  for (int i = tid; i < E; i += THREADS) s_thr[i] = a.sp.ev[u * ev_stride(P) + i] - i;
   if (pt_lds)
-    for (int i = tid; i <= A; i += 256) s_pt[i] = ptg[i];
+    for (int i = tid; i <= A; i += THREADS) s_pt[i] = ptg[i];
   __syncthreads();
   const int esz = g.dtype == GP_BF16 ? 2 : 4;
   const int64_t hoff = ((int64_t)l * g.s_layer + (int64_t)kvh * g.s_head) * esz;
@@ -503,9 +505,15 @@ hipError_t launch_compact_move(const Geo& g, const gp_pages& pg, const ScratchPt
   const int cpr = g.d * esz / 16;  // 16-byte pieces per row: 8, 16 or 32
   const dim3 grid(2 * units);      // K and V block of each unit, adjacent
   // A grid that fits in one round of resident blocks (8 per CU) is latency-bound: take
-  // the form with all of a step's loads in flight.
+  // the form with all of a step's loads in flight; with at most one block per CU, in
+  // blocks of 1024 threads (rows of up to 256 bytes: wider rows would not fit the
+  // registers of 16 waves per CU).
   const bool small = 2 * (int64_t)units <= kResidentGatherBlocks;
-  if (cpr == 8) {
+  const bool tiny = 2 * (int64_t)units <= kResidentGatherBlocks / 8 && cpr <= 16;
+  if (tiny) {
+    if (cpr == 8) hipLaunchKernelGGL((gather_kernel<8, true, 1024>), grid, dim3(1024), 0, st, a);
+    else hipLaunchKernelGGL((gather_kernel<16, true, 1024>), grid, dim3(1024), 0, st, a);
+  } else if (cpr == 8) {
     if (small) hipLaunchKernelGGL((gather_kernel<8, true>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((gather_kernel<8, false>), grid, dim3(256), 0, st, a);
   } else if (cpr == 16) {

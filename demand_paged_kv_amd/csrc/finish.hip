@@ -28,6 +28,8 @@
 //           tail, which only a near-tie allows) are refined by the whole block from
 //           the logits in global memory, filtered to b*.
 // All decisions are exact for the float32 logits the scan produced.
+#include <algorithm>
+
 #include "device_util.h"
 #include "gp_internal.h"
 #include "logit_mfma.h"
@@ -741,7 +743,100 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void f
   finish_unit<KCAP>(f, rank, l, kvh, lds);
 }
 
+// Batches with fewer units than resident blocks (a few requests, or one layer): one block
+// per unit would leave most of the chip idle and make each block's walk through a long
+// unit a latency chain.  Here a unit's 16-token steps are cut into `parts` contiguous
+// ranges, one block (four waves, the fused kernel's steps, staging and logit layout) per
+// range; the parts' row maxima meet in the statistics through float atomics (set to -inf
+// first), and finish_kernel then selects from the logits.
+
+// Row maxima to -inf for every (entry, layer, query head, summary) of the batch.
+__global__ __launch_bounds__(256) void init_max_kernel(ScratchPtrs sp, int64_t rows) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows; i += (int64_t)gridDim.x * 256)
+    sp.stats[i * 2] = -INFINITY;
+}
+
+// Float max through integer atomics: non-negative floats order like their bit patterns
+// as signed integers, negative ones in reverse as unsigned integers.  (-0 is made +0
+// first, so that it is not taken for the smallest value.)
+__device__ __forceinline__ void atomic_max_f32(float* p, float v) {
+  v += 0.f;
+  if (v >= 0.f)
+    atomicMax(reinterpret_cast<int*>(p), __float_as_int(v));
+  else
+    atomicMin(reinterpret_cast<unsigned*>(p), __float_as_uint(v));
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void split_logit_kernel(ScanArgs s,
+                                                                                                 int parts) {
+  __shared__ float s_stage[4 * kStageBytes / sizeof(float)];
+  __shared__ float s_mw[4][kDists];
+  const Geo& g = s.g;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int unit = blockIdx.x / parts;
+  const int part = blockIdx.x - unit * parts;
+  const int upr = g.L * g.Hkv;
+  const int rank = unit / upr;
+  const int rem = unit - rank * upr;
+  const int l = rem / g.Hkv;
+  const int kvh = rem - l * g.Hkv;
+  const int b = s.sp.order[rank];
+  if (s.sp.flags[b]) return;
+  const int n = s.sp.n_tok[b];
+  const int steps = (n + kMfmaTok - 1) / kMfmaTok;
+  const int p0 = (int)((int64_t)steps * part / parts);
+  const int p1 = (int)((int64_t)steps * (part + 1) / parts);
+  if (p0 >= p1) return;  // the whole block: nothing of this unit falls in the part
+  const int r = g.req_ids[b];
+  const int32_t* pt = g.page_table + (int64_t)r * g.max_pages;
+  MfmaSummaries<D> A;
+  A.load(s, r, l, kvh, lane);
+  const int s0 = p0 + (p1 - p0) * wave / 4;
+  const int s1 = p0 + (p1 - p0) * (wave + 1) / 4;
+  float* lg = s.sp.logits + (s.sp.tok_off[b] * g.L * g.Hkv + (int64_t)(l * g.Hkv + kvh) * logit_rows(n)) * kDists;
+  float* stage = s_stage + wave * (kStageBytes / sizeof(float));
+  f32x4_t mx = mfma_logit_steps<D>(s, A, pt, n, l, kvh, s0, s1, lg, stage, lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v = mx[i];
+    v = fmaxf(v, __shfl_xor(v, 1, 64));
+    v = fmaxf(v, __shfl_xor(v, 2, 64));
+    v = fmaxf(v, __shfl_xor(v, 4, 64));
+    v = fmaxf(v, __shfl_xor(v, 8, 64));
+    mx[i] = v;
+  }
+  if (lane == 0 || lane == 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_mw[wave][4 * (lane >> 4) + i] = mx[i];
+  }
+  __syncthreads();
+  if (tid < kDists && row_real(tid, g.G)) {
+    const float m = fmaxf(fmaxf(s_mw[0][tid], s_mw[1][tid]), fmaxf(s_mw[2][tid], s_mw[3][tid]));
+    const int h = kvh * g.G + (tid >> 1);
+    atomic_max_f32(&s.sp.stats[((((int64_t)b * g.L + l) * g.Hq + h) * 2 + (tid & 1)) * 2], m);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_split_scan(const ScanArgs& s, const FinishArgs& f, int parts, hipStream_t st) {
+  const Geo& g = s.g;
+  const int64_t units = (int64_t)g.n_req * g.L * g.Hkv;
+  const int64_t rows = (int64_t)g.n_req * g.L * g.Hq * 2;
+  hipLaunchKernelGGL(init_max_kernel, dim3((unsigned)std::min<int64_t>((rows + 255) / 256, 1024)), dim3(256), 0,
+                     st, s.sp, rows);
+  const dim3 grid((unsigned)(units * parts)), block(256);
+  if (g.d == 128)
+    hipLaunchKernelGGL((split_logit_kernel<128>), grid, block, 0, st, s, parts);
+  else
+    hipLaunchKernelGGL((split_logit_kernel<64>), grid, block, 0, st, s, parts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_finish(f, st);
+}
 
 hipError_t launch_fused_scan(const ScanArgs& s, const FinishArgs& f, hipStream_t st) {
   const int64_t units = (int64_t)f.g.n_req * f.g.L * f.g.Hkv;

@@ -182,6 +182,10 @@ struct ScanArgs {
 // bf16 keys in pages of a multiple of 16 tokens: logits and working sets in one kernel.
 constexpr int kFusedPageMultiple = 16;
 hipError_t launch_fused_scan(const ScanArgs& s, const FinishArgs& f, hipStream_t st);
+// The same for batches of at most kSplitUnits units: each unit's steps in `parts` blocks,
+// then finish_kernel.
+constexpr int64_t kSplitUnits = 512;
+hipError_t launch_split_scan(const ScanArgs& s, const FinishArgs& f, int parts, hipStream_t st);
 
 hipError_t launch_decide(const int32_t* ws, const int32_t* req_ids, int32_t n_req, int32_t L,
                          int32_t Hq, int32_t tau, const gp_pages& pg, int32_t P, int32_t policy,

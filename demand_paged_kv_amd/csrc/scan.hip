@@ -19,6 +19,8 @@
 //                  running max to the statistics.
 //   finish_kernel  one block per unit (finish.hip): exact Top-p working sets of the 8
 //                  logit rows and the unit's keep-set, from two reads of the logits.
+#include <algorithm>
+
 #include "device_util.h"
 #include "gp_internal.h"
 #include "kv_chunk.h"
@@ -295,7 +297,12 @@ hipError_t launch_scan(const Geo& g, const ScratchPtrs& sp, int64_t max_tokens,
   if (e != hipSuccess) return e;
   const int64_t units = (int64_t)g.n_req * g.L * g.Hkv;
   FinishArgs f{g, sp, top_p, n_local, shrink, ws_out, stats_out};
-  if (g.dtype == GP_BF16 && g.P % kFusedPageMultiple == 0) return launch_fused_scan(a, f, st);
+  if (g.dtype == GP_BF16 && g.P % kFusedPageMultiple == 0) {
+    // Fewer units than the 1024 fused blocks resident at once (4 per CU): split each unit
+    // into parts so that about 1024 blocks stream K, at most 8 parts per unit.
+    if (units <= kSplitUnits) return launch_split_scan(a, f, (int)std::min<int64_t>(8, 1024 / units), st);
+    return launch_fused_scan(a, f, st);
+  }
   if (g.dtype == GP_BF16) {
     e = g.d == 128 ? launch_logits<true, 128>(a, units, st) : launch_logits<true, 64>(a, units, st);
   } else {

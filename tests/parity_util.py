@@ -238,6 +238,30 @@ def check_pool(st, before: dict, decision: np.ndarray, slots: np.ndarray):
     assert top + np.count_nonzero(refs) == rc.size
 
 
+def pad_with_empty(wl, extra: int):
+    """``wl`` with ``extra`` more requests that hold only an empty write page (n = 0, not at
+    a boundary), each on a page added to the pool: input construction that makes a batch
+    larger in (request, layer, KV head) units without adding work or changing the real
+    requests."""
+    if extra <= 0:
+        return wl
+    B0, np0 = wl.B, wl.num_pages
+    table = np.full((B0 + extra, wl.max_pages), -1, np.int32)
+    table[:B0] = wl.page_table
+    table[B0:, 0] = np.arange(np0, np0 + extra, dtype=np.int32)
+    zi = np.zeros(extra, np.int32)
+    empty = np.zeros((wl.L, wl.Hkv, 0, wl.d), wl.k_rows[0].dtype)
+    zs = np.zeros((extra,) + wl.sum_s.shape[1:], np.float32)
+    return dataclasses.replace(
+        wl, num_pages=np0 + extra, page_table=table, n_alloc=np.concatenate([wl.n_alloc, zi]),
+        fill=np.concatenate([wl.fill, zi]), pos=np.concatenate([wl.pos, zi]),
+        refcount=np.concatenate([wl.refcount, np.ones(extra, wl.refcount.dtype)]),
+        free_stack=np.concatenate([wl.free_stack, np.zeros(extra, wl.free_stack.dtype)]),
+        k_rows=list(wl.k_rows) + [empty] * extra, v_rows=list(wl.v_rows) + [empty] * extra,
+        sum_s=np.concatenate([wl.sum_s, zs]), sum_l=np.concatenate([wl.sum_l, zs]),
+        regime=None if wl.regime is None else np.concatenate([wl.regime, zi]))
+
+
 def run_step_gpu(wl, sum_s=None, sum_l=None, slots=None, max_req=None, params=None, tokens_budget=None):
     """Upload ``wl``, run one boundary batch through the C ABI, synchronise."""
     from demand_paged_kv_amd import binding as Bd

@@ -201,6 +201,28 @@ def test_direct_cases(name, kw):
     _say(name, rep, res.counters, "logit/probability errors", errs)
 
 
+# The same cases on the fused scan kernel: small batches (at most 512 units) take the split
+# logit kernel plus a selection kernel, so each bf16 case with pages of a multiple of 16
+# tokens is run again with empty requests added until the batch has more units than that.
+FUSED_CASES = [c for c in CASES if c[1].get("dtype", "bf16") == "bf16" and c[1].get("P", 16) % 16 == 0]
+SPLIT_UNITS = 512
+
+
+@pytest.mark.parametrize("name,kw", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_direct_cases_fused_kernel(name, kw):
+    from tests.parity_util import pad_with_empty
+    wl = SW.direct_case(seed=zlib.crc32(name.encode()) % 10000, name=name, **kw)
+    b0, per = wl.B, wl.L * wl.Hkv
+    wl = pad_with_empty(wl, -(-(SPLIT_UNITS + 1) // per) - b0)
+    assert wl.B * per > SPLIT_UNITS
+    _say(f"[case] {name} fused: B={wl.B} ({b0} with tokens) tokens={wl.total_tokens()}")
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, wl.params)
+    st, out, eng = run_step_gpu(wl)
+    rep = compare_step(wl, np.arange(wl.B), st, out, res, wl.params["n_local"])
+    errs = compare_logits(eng, wl, range(b0))
+    _say(name, "fused", rep, res.counters, "logit/probability errors", errs)
+
+
 def test_rope_positions_clamped_to_the_table():
     """Positions beyond the caller's rotation table use its last row: the scan on a table
     cut short matches the oracle at the clamped positions (full table, same rows)."""
@@ -325,13 +347,27 @@ PLANTED += [
 @pytest.mark.parametrize("name,fns,params,dtype", [c + ("f32",) for c in PLANTED] + [c + ("bf16",) for c in PLANTED_BF16],
                          ids=[c[0] for c in PLANTED] + [c[0] for c in PLANTED_BF16])
 def test_planted_logits(name, fns, params, dtype):
+    _planted(name, fns, params, dtype, False)
+
+
+@pytest.mark.parametrize("name,fns,params", PLANTED_BF16, ids=[c[0] for c in PLANTED_BF16])
+def test_planted_logits_fused_kernel(name, fns, params):
+    """The bf16 planted cases on the fused scan kernel (empty requests added)."""
+    _planted(name, fns, params, "bf16", True)
+
+
+def _planted(name, fns, params, dtype, fused):
     wl = SW.planted_logits_case(zlib.crc32(name.encode()) % 10000, fns, params=params, name=name, dtype=dtype)
-    _say(f"[planted] {name} n={[wl.n(b) for b in range(wl.B)]}")
+    b0 = wl.B
+    if fused:
+        from tests.parity_util import pad_with_empty
+        wl = pad_with_empty(wl, -(-(SPLIT_UNITS + 1) // (wl.L * wl.Hkv)) - wl.B)
+    _say(f"[planted] {name} n={[wl.n(b) for b in range(b0)]} batch {wl.B}")
     res = O.boundary_step(wl, wl.sum_s, wl.sum_l, wl.params)
     st, out, eng = run_step_gpu(wl)
     rep = compare_step(wl, np.arange(wl.B), st, out, res, wl.params["n_local"])
-    errs = compare_logits(eng, wl, range(wl.B))
-    _say(name, rep, res.counters, "W", res.W[:, 0, 0].tolist(), "logit/probability errors", errs)
+    errs = compare_logits(eng, wl, range(b0))
+    _say(name, rep, res.counters, "W", res.W[:b0, 0, 0].tolist(), "logit/probability errors", errs)
 
 
 @pytest.mark.parametrize("policy", ["growpage", "random", "inverse", "always_compact", "shrink"])
@@ -426,10 +462,12 @@ def test_contiguous_pools():
     _say(name, rep, res.counters)
 
 
-def test_token_budget_overflow():
+@pytest.mark.parametrize("kernel", ["split", "fused"])
+def test_token_budget_overflow(kernel):
     """A batch larger than the scratch's token budget: the entries that fit (a prefix in
     batch order) behave as the oracle's step on them alone; the rest are flagged
-    GP_REQ_OVERFLOW, report working sets of -1 and are left untouched."""
+    GP_REQ_OVERFLOW, report working sets of -1 and are left untouched.  ``fused``: empty
+    requests added after them make the batch large enough for the fused scan kernel."""
     import dataclasses
     from demand_paged_kv_amd import binding as Bd
     from demand_paged_kv_amd.engine import BoundaryEngine
@@ -437,6 +475,10 @@ def test_token_budget_overflow():
     name = "token_overflow"
     wl = SW.direct_case(seed=zlib.crc32(name.encode()) % 10000, B=6, L=2, Hq=8, Hkv=2, d=64, P=16,
                         ctx=(100, 400), grow_frac=0.2, spare_pages=30, name=name)
+    b0 = wl.B
+    if kernel == "fused":
+        from tests.parity_util import pad_with_empty
+        wl = pad_with_empty(wl, -(-(SPLIT_UNITS + 1) // (wl.L * wl.Hkv)) - wl.B)
     j = 3   # the fitting prefix holds a grow and two compactions
     budget = sum(wl.n(b) for b in range(j))
     sub = dataclasses.replace(wl, page_table=wl.page_table[:j], n_alloc=wl.n_alloc[:j], fill=wl.fill[:j],
@@ -453,7 +495,9 @@ def test_token_budget_overflow():
     dec = out.decision.cpu().numpy()
     table = st.page_table.cpu().numpy()
     for b in range(j, wl.B):
-        assert status[b] == Bd.GP_REQ_OVERFLOW and dec[b] == Bd.GP_DECISION_COMPACT, (b, status[b], dec[b])
+        # the added empty requests are also not at a boundary
+        want = Bd.GP_REQ_OVERFLOW | (Bd.GP_REQ_NOT_AT_BOUNDARY if b >= b0 else 0)
+        assert status[b] == want and dec[b] == Bd.GP_DECISION_COMPACT, (b, status[b], dec[b])
         assert np.all(ws[b] == -1)
         assert int(st.n_alloc[b]) == int(wl.n_alloc[b]) and int(st.fill[b]) == int(wl.fill[b])
         assert np.array_equal(table[b], wl.page_table[b])
