@@ -7,7 +7,9 @@
 //                longest-first order of the entries.
 // Then, for bf16 keys in pages of a multiple of 16 tokens, fused_scan_kernel (finish.hip):
 // one block per (entry, layer, KV head) "unit" computes the unit's logits on the matrix
-// cores (logit_mfma.h) and selects from them.  Otherwise two kernels:
+// cores (logit_mfma.h) and selects from them; a batch of at most kSplitUnits units runs
+// the same logit steps split over several blocks per unit (split_logit_kernel) and then
+// finish_kernel.  Otherwise two kernels:
 //   logit_kernel   one wave per unit, launched longest-first.  The wave streams the
 //                  unit's K rows through the page table once; 16 lanes share a token row
 //                  (each holds D/16 contiguous elements), every lane keeps the matching
