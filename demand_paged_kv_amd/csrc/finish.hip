@@ -581,6 +581,10 @@ __device__ __forceinline__ void finish_unit(const FinishArgs& a, int rank, int l
     }
     __syncthreads();
     const int cnt = s_kcount;
+    // every thread holds the count before the next round adds to it: without this
+    // barrier a wave that runs ahead could raise it under a slower one's read, and the
+    // waves would disagree on entering the block-wide selection below
+    __syncthreads();
     if (cnt > kcap - 256) {  // the next round might not fit: keep the E smallest
       const u64 K = block_kth_smallest(kbuf, cnt, E, sel_hist, s_x, tid);
       if (tid == 0) s_c2 = 0;
