@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 4 GiB device copy (HBM counter calibration)")
     ap.add_argument("--workload", choices=("boundary_sweep", "decode_loop", "prefix_share", "policies", "overlap",
-                                           "one_layer"),
+                                           "one_layer", "single_request"),
                     default="boundary_sweep",
                     help="boundary_sweep (default, the headline line); decode_loop (the 36-layer decode "
                          "loop: 128 requests x 4096 steps) or prefix_share (256 requests x 36 layers, page "
@@ -62,7 +62,9 @@ def parse():
                          "correlation with the later working set) or overlap (decode attention with the "
                          "boundary engine serial vs on a second stream) or one_layer (16 requests, one layer, "
                          "summaries from 256 decode queries: a batch small enough to be bound by launch "
-                         "latency), each reported on its own line")
+                         "latency) or single_request (the boundary of one request, 36 layers, at the "
+                         "pages' operating point and at page 16, 4K and 16K tokens: the latency of the "
+                         "boundaries that come one at a time), each reported on its own line")
     ap.add_argument("--decode-steps", type=int, default=4096)
     ap.add_argument("--graphs", action="store_true",
                     help="decode_loop: replay each step from HIP graphs (one launch per step) "
@@ -126,6 +128,9 @@ def main():
         return
     if args.workload == "one_layer":
         one_layer(args)
+        return
+    if args.workload == "single_request":
+        single_request(args)
         return
     import numpy as np
     import torch
@@ -306,6 +311,72 @@ def one_layer(args):
                       "summary_update_ms_per_query": round(ema_ms, 4),
                       "decisions": {"grow": int(c["grows"]), "compact": int(c["compacts"])},
                       "counters": c}), flush=True)
+
+
+def single_request(args):
+    """The boundary batch of one request (36 layers, 32/8 heads, d 128, bf16, a concentrating
+    request, so it compacts), timed per call like the sweep (state restored between steps):
+    at the pages' operating point (KV block 256, p 0.99, quota 64) with about 4K and 16K
+    tokens, and at page 16.  With the pages' block size a request reaches a boundary once
+    every 256 decode steps, so boundaries mostly come one request at a time; 288 units
+    leave most of the chip to the latency of each unit's walk."""
+    import numpy as np
+    import torch
+
+    from demand_paged_kv_amd import binding as Bd
+    from demand_paged_kv_amd.engine import BoundaryEngine
+    from synth import gpu_workloads as GW
+    from synth import workloads as SW
+
+    Bd.load()
+    L = 36
+    names = ("scan", "decide", "compact_prepare", "compact_move")
+    cases = []
+    for P, ctx in ((256, 16000), (256, 4000), (16, 16000), (16, 4000)):
+        prm = dict(SW.PARAMS_PAPER) if P == 256 else dict(SW.PARAMS_DEFAULT)
+        gw = GW.boundary_sweep(seed=args.seed + 200, B=1, L=L, P=P, num_pages=ctx // P + 10, ctx=(ctx, ctx),
+                               grow_frac=0.0, params=prm, name="single_request",
+                               contiguous=not args.ordinary_pools)
+        st = gw.st
+        eng = BoundaryEngine(st, 1, gw.total_tokens(), Bd.params_from(gw.params))
+        req = torch.zeros(1, dtype=torch.int32, device="cuda")
+        backup = GW.StateBackup(st)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        times = []
+        for i in range(args.warmup + args.steps):
+            backup.restore()
+            torch.cuda.synchronize()
+            ev[0].record()
+            eng.scan(req)
+            ev[1].record()
+            eng.decide(req)
+            ev[2].record()
+            eng.compact_prepare(req)
+            ev[3].record()
+            eng.compact_move(req)
+            ev[4].record()
+            torch.cuda.synchronize()
+            if i >= args.warmup:
+                times.append([ev[k].elapsed_time(ev[k + 1]) for k in range(4)])
+        med = np.median(np.array(times), axis=0)
+        c = dict(zip(Bd.COUNTER_NAMES, [int(x) for x in eng.out.counters.cpu().numpy()]))
+        n = gw.total_tokens()
+        scan_b = L * st.Hkv * n * st.d * 2
+        move_b = c["moved_rows"] * 4 * st.d * 2
+        case = {"page_size": P, "tokens": n, "top_p": gw.params["top_p"], "n_local": gw.params["n_local"],
+                "ms": {k: round(float(v), 4) for k, v in zip(names, med)}, "total_ms": round(float(med.sum()), 4),
+                "scan_GBps": round(float(scan_b / med[0] / 1e6), 1),
+                "move_GBps": round(float(move_b / max(med[3], 1e-9) / 1e6), 1),
+                "decision": "compact" if c["compacts"] else "grow"}
+        log(f"single request P={P} n={n}: {case}")
+        cases.append(case)
+        del eng, st, gw, backup
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "boundary batch latency of one request (ms, median of the timed steps)",
+                      "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
+                      "config": {"workload": "single_request: 1 request x 36 layers, 32q/8kv heads, d128, bf16 K/V, "
+                                             "concentrating (it compacts)", "seed": args.seed + 200},
+                      "cases": cases, "data": "synthetic"}), flush=True)
 
 
 def placements(args):
