@@ -762,8 +762,10 @@ __global__ __launch_bounds__(256) void init_max_kernel(ScratchPtrs sp, int64_t r
 
 // Float max through integer atomics: non-negative floats order like their bit patterns
 // as signed integers, negative ones in reverse as unsigned integers.  (-0 is made +0
-// first, so that it is not taken for the smallest value.)
+// first, so that it is not taken for the smallest value; a NaN is ignored, as fmaxf
+// ignores it in the fused kernel's combine.)
 __device__ __forceinline__ void atomic_max_f32(float* p, float v) {
+  if (v != v) return;
   v += 0.f;
   if (v >= 0.f)
     atomicMax(reinterpret_cast<int*>(p), __float_as_int(v));
