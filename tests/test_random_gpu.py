@@ -75,3 +75,57 @@ def test_random_batch(seed):
     rep = compare_step(wl, np.arange(wl.B), st, out, res, wl.params["n_local"])
     errs = compare_logits(eng, wl, range(wl.B))
     print(f"[random] seed {seed}: {res.counters} {rep} logit/probability errors {errs}", flush=True)
+
+
+# Larger batches (8-24 requests x 2-4 layers x 8 KV heads: 128-768 units), bf16 keys in pages
+# of 16-256 tokens: both forms of the matrix-core scan, a unit's steps split over several
+# blocks (at most 512 units) and one fused block per unit (more).
+LARGE_SEEDS = list(range(30000, 30040))
+
+
+def _draw_large(seed):
+    rng = np.random.default_rng(seed)
+    G = int(rng.choice([1, 2, 4, 4]))
+    Hkv = 8
+    d = int(rng.choice([64, 128]))
+    P = int(rng.choice([16, 16, 32, 64, 128, 256]))
+    B = int(rng.integers(8, 25))
+    L = int(rng.integers(2, 5))
+    lo = int(rng.integers(1, 1500))
+    hi = lo + int(rng.integers(0, 3000))
+    prefix_groups = int(rng.integers(0, 3)) if rng.random() < 0.4 else 0
+    prefix_pages = int(rng.integers(1, 4)) if prefix_groups else 0
+    fill = None
+    if rng.random() < 0.3:
+        fill = np.where(rng.random(B) < 0.7, P, rng.integers(0, P, B)).astype(np.int32)
+    policy = str(rng.choice(["growpage"] * 5 + ["shrink", "inverse", "random", "always_compact"]))
+    params = dict(beta_s=0.9, beta_l=0.999, top_p=float(rng.choice([0.5, 0.9, 0.95, 0.99, 0.999])),
+                  tau=int(rng.choice([0, 0, 0, 50, -50])), n_local=int(rng.choice([0, 4, 16, 64])))
+    kw = dict(B=B, L=L, Hq=G * Hkv, Hkv=Hkv, d=d, P=P, dtype="bf16", ctx=(lo, hi),
+              spare_pages=int(rng.integers(0, 60)), grow_frac=float(rng.uniform(0, 1)),
+              rope=bool(rng.random() < 0.85), prefix_groups=prefix_groups, prefix_pages=prefix_pages,
+              fill=fill, params=params)
+    wl = SW.direct_case(seed=seed, name=f"large{seed}", **kw)
+    u = rng.random(B).astype(np.float32)
+    return wl, policy, u, float(rng.uniform(0.1, 0.9))
+
+
+@pytest.mark.parametrize("seed", LARGE_SEEDS)
+def test_random_large_batch(seed):
+    from demand_paged_kv_amd import binding as Bd
+    from demand_paged_kv_amd.engine import BoundaryEngine
+    wl, policy, u, grow_prob = _draw_large(seed)
+    prm = dict(wl.params, policy=policy, rand_u=u, grow_prob=grow_prob)
+    print(f"[random-large] seed {seed}: B={wl.B} L={wl.L} Hq={wl.Hq} d={wl.d} P={wl.P} "
+          f"units={wl.B * wl.L * wl.Hkv} tokens={wl.total_tokens()} policy={policy}", flush=True)
+    res = O.boundary_step(wl, wl.sum_s, wl.sum_l, prm)
+    if res.ambiguous.any():
+        pytest.skip("the oracle finds a decision ambiguous (delta within rounding of tau)")
+    st = SD.upload(wl, "cuda")
+    eng = BoundaryEngine(st, wl.B, wl.total_tokens(), Bd.params_from(prm))
+    eng.set_policy(policy, torch.as_tensor(u, device="cuda"), grow_prob)
+    out = eng.step(torch.arange(wl.B, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    rep = compare_step(wl, np.arange(wl.B), st, out, res, wl.params["n_local"])
+    errs = compare_logits(eng, wl, range(min(wl.B, 3)))
+    print(f"[random-large] seed {seed}: {res.counters} {rep} logit/probability errors {errs}", flush=True)
